@@ -1,0 +1,192 @@
+"""Float64 CPU oracle of Sol-Attn block-sparse attention (test infrastructure only).
+
+What the pages fix
+------------------
+Sol-Attn is the largest single source of the Sol-H3 runtime's speed-up: a sparse
+attention that decides, per query, which parts of the attention computation
+matter, and that needs no retraining ("Videomodel MiniMax-H3 rendert sneller dan
+afspelen", section "Waar de snelheidswinst vandaan komt").  The same section says
+the *preparation* of the sparse attention was made faster, i.e. there is a
+selection step before the attention proper.  In the two-stage schedule it runs in
+the high-resolution refinement steps ("NVIDIA Adds Two-Stage Generation for
+MiniMax H3 ...", first paragraph).
+
+The concrete reading implemented (the pages give no formula)
+-----------------------------------------------------------
+* tokens are frame-major; the sequence is cut into contiguous blocks of Bs tokens;
+* every query block and key block is mean-pooled (block sum / Bs);
+* pooled score of (query block i, key block j) is r_ij / sqrt(d), r_ij = Qbar_i . Kbar_j;
+* each query block keeps the k key blocks with the largest score, ties going to
+  the lower key-block index; indices are emitted in ascending order;
+* every query of block i then attends with exact softmax(q k^T / sqrt(d)) over
+  the union of the selected key blocks' tokens, with no mask.
+
+Ranking uses the unscaled r_ij: multiplying by the positive constant 1/sqrt(d)
+preserves the order in exact arithmetic, and not applying it avoids creating
+rounding ties.  Everything is float64; inputs are the exact widenings of the
+stored bf16/fp32 values.
+
+Every function below is the definition written out step by step.  Library
+primitives used as single steps: numpy sum, lexsort and matmul.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = ["widen", "pool", "block_scores", "select", "select_from_scores", "attend",
+           "attend_block", "selection_margins", "run"]
+
+
+def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored inputs: bf16 given as uint16 bit patterns, or float32."""
+    if dtype == "bf16":
+        bits = np.asarray(stored, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "fp32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def pool(X: np.ndarray, block: int) -> np.ndarray:
+    """Block mean: [..., L, d] -> [..., L/block, d], Xbar_i = (sum of the block's rows) / block."""
+    *lead, L, d = X.shape
+    if L % block:
+        raise ValueError("L must be a multiple of the block size")
+    nb = L // block
+    sums = X.reshape(*lead, nb, block, d).sum(axis=-2)
+    return sums / block
+
+
+def block_scores(Qbar: np.ndarray, Kbar: np.ndarray, chunk: int = 64) -> np.ndarray:
+    """r_ij = sum_e Qbar_ie * Kbar_je for all block pairs: [..., nq, d] x [..., nk, d] -> [..., nq, nk].
+
+    Each r_ij is evaluated the same way (elementwise product, then a sum over e),
+    so two identical key blocks always get identical scores.
+    """
+    *lead, nq, d = Qbar.shape
+    nk = Kbar.shape[-2]
+    r = np.empty((*lead, nq, nk), dtype=np.float64)
+    for i0 in range(0, nq, chunk):
+        i1 = min(nq, i0 + chunk)
+        prod = Qbar[..., i0:i1, None, :] * Kbar[..., None, :, :]
+        r[..., i0:i1, :] = prod.sum(axis=-1)
+    return r
+
+
+def select_from_scores(r: np.ndarray, topk: int) -> np.ndarray:
+    """Per row of r (the last axis indexes key blocks j): the first `topk` j in the order
+    (r desc, j asc), returned in ascending j.  int32 [..., topk]."""
+    *lead, nk = r.shape
+    if not 1 <= topk <= nk:
+        raise ValueError("topk out of range")
+    flat = r.reshape(-1, nk)
+    out = np.empty((flat.shape[0], topk), dtype=np.int32)
+    j = np.arange(nk)
+    for row in range(flat.shape[0]):
+        order = np.lexsort((j, -flat[row]))     # primary: -r ascending, secondary: j ascending
+        out[row] = np.sort(order[:topk])
+    return out.reshape(*lead, topk)
+
+
+def select(Qbar: np.ndarray, Kbar: np.ndarray, topk: int) -> np.ndarray:
+    """Top-k key blocks per query block by pooled score (see module docstring)."""
+    return select_from_scores(block_scores(Qbar, Kbar), topk)
+
+
+def attend_block(Qi: np.ndarray, K: np.ndarray, V: np.ndarray, sel_i: np.ndarray, block: int,
+                 scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact softmax attention of the rows of one query block over its selected key blocks.
+
+    Qi [Bs, d]; K, V [L, d] of the same (b, h); sel_i [k] key-block indices.
+    Returns (O_i [Bs, d], lse_i [Bs]) with lse = m + ln(sum exp(z - m)).
+    """
+    d = K.shape[-1]
+    rows = (sel_i[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    Kc = K[rows]
+    Vc = V[rows]
+    z = (Qi @ Kc.T) * scale                  # [Bs, k*Bs]
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    l = p.sum(axis=1, keepdims=True)
+    O = (p @ Vc) / l
+    lse = (m + np.log(l))[:, 0]
+    return O, lse
+
+
+def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, block: int,
+           scale: Optional[float] = None, qblocks: Optional[np.ndarray] = None):
+    """Block-sparse attention for [..., L, d] inputs and sel [..., nB, k].
+
+    scale defaults to 1/sqrt(d).  `qblocks` (optional) restricts the query blocks
+    computed (same set for every leading index); other rows of O are NaN.
+    Returns (O [..., L, d], lse [..., L]).
+    """
+    *lead, L, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nb = L // block
+    Qf = Q.reshape(-1, L, d)
+    Kf = K.reshape(-1, L, d)
+    Vf = V.reshape(-1, L, d)
+    sf = sel.reshape(-1, nb, sel.shape[-1])
+    O = np.full(Qf.shape, np.nan)
+    lse = np.full(Qf.shape[:2], np.nan)
+    blocks = range(nb) if qblocks is None else qblocks
+    for bh in range(Qf.shape[0]):
+        for i in blocks:
+            s = slice(i * block, (i + 1) * block)
+            O[bh, s], lse[bh, s] = attend_block(Qf[bh, s], Kf[bh], Vf[bh], sf[bh, i], block, scale)
+    return O.reshape(*lead, L, d), lse.reshape(*lead, L)
+
+
+def selection_margins(Qbar: np.ndarray, Kbar: np.ndarray, topk: int):
+    """Certificate that the float64 selection equals the exact-arithmetic selection.
+
+    For every row: gap = r_(k) - r_(k+1) between the k-th and (k+1)-th largest
+    scores (inf when k = nB), and a rounding bound on |computed r - exact r| of
+    2 * gamma_d * sum_e |Qbar_ie||Kbar_je| with gamma_d = d*u/(1-d*u), u = 2^-53
+    (the standard bound for a d-term dot product; the factor 2 covers the two
+    scores being compared).  A row with gap == 0 is an exact tie, resolved by
+    index; a row with 0 < gap <= bound is ambiguous.
+
+    Returns (min relative gap over rows with gap > 0, number of ambiguous rows,
+    number of rows whose k-th/(k+1)-th scores tie exactly).
+    """
+    r = block_scores(Qbar, Kbar)
+    mag = block_scores(np.abs(Qbar), np.abs(Kbar))
+    d = Qbar.shape[-1]
+    u = 2.0 ** -53
+    gamma = d * u / (1 - d * u)
+    *lead, nq, nk = r.shape
+    rf = r.reshape(-1, nk)
+    mf = mag.reshape(-1, nk)
+    min_rel = math.inf
+    ambiguous = 0
+    ties = 0
+    if topk >= nk:
+        return math.inf, 0, 0
+    for row in range(rf.shape[0]):
+        srt = np.sort(rf[row])[::-1]
+        gap = srt[topk - 1] - srt[topk]
+        bound = 2.0 * gamma * mf[row].max()
+        if gap == 0:
+            ties += 1
+            continue
+        if gap <= bound:
+            ambiguous += 1
+        scale_row = max(abs(srt[topk - 1]), abs(srt[topk]), 1e-300)
+        min_rel = min(min_rel, gap / scale_row)
+    return min_rel, ambiguous, ties
+
+
+def run(q_stored, k_stored, v_stored, dtype: str, block: int, topk: int,
+        qblocks: Optional[np.ndarray] = None):
+    """Whole path on stored inputs [B,H,L,d]: returns dict(qbar, kbar, idx, out, lse)."""
+    Q, K, V = widen(q_stored, dtype), widen(k_stored, dtype), widen(v_stored, dtype)
+    qbar, kbar = pool(Q, block), pool(K, block)
+    idx = select(qbar, kbar, topk)
+    out, lse = attend(Q, K, V, idx, block, qblocks=qblocks)
+    return dict(qbar=qbar, kbar=kbar, idx=idx, out=out, lse=lse)
