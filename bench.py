@@ -1,0 +1,187 @@
+"""Benchmark of the Sol-Attn hot path on one MI355X.
+
+A step = one pass of the whole path over one batch: sol_attn_pool -> sol_attn_select
+-> sol_attn_fwd, on seeded synthetic Q/K/V already resident in HBM.  Default workload:
+the 1344x768 refinement stage (16 latent frames x 48 x 84 = 64,512 tokens, B=1,
+H=40, d=128, bf16, 128-token blocks, top-76 of 504 key blocks).
+
+Prints ONE JSON line.  `value` = effective TFLOP/s of the whole step, counting the
+two contractions over the selected key blocks only (4*B*H*L*k*Bs*d flops per step).
+`roofline` covers the dominant kernel (sol_attn_fwd): algorithmic flops per launch
+divided by its average launch time measured with HIP events on its stream.
+`cpu_baseline` times the float64 CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+
+# HBM traffic of one sol_attn_fwd launch on the headline workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) scaled by the copy-kernel
+# calibration factor; None until measured for the current kernel.
+FWD_TRAFFIC_BYTES = None
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="refine_1344x768")
+    p.add_argument("--topk", type=int, default=None, help="override k (e.g. all blocks for a dense run)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-blocks", type=int, default=24,
+                   help="query blocks of one head the CPU oracle attends for its baseline")
+    return p.parse_args()
+
+
+def cpu_baseline(wl, q, k, v, topk, n_blocks_sample):
+    """Time the float64 oracle (pool + select + attend) on head 0 of the workload,
+    attending `n_blocks_sample` evenly spaced query blocks of that head."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    Q = oracle.widen(q[0, 0], wl.dtype)
+    K = oracle.widen(k[0, 0], wl.dtype)
+    V = oracle.widen(v[0, 0], wl.dtype)
+    qb, kb = oracle.pool(Q, wl.block), oracle.pool(K, wl.block)
+    blocks = np.linspace(0, wl.n_blocks - 1, n_blocks_sample).astype(int)
+    r = oracle.block_scores(qb[blocks], kb)
+    idx = oracle.select_from_scores(r, topk)
+    for n, i in enumerate(blocks):
+        s = slice(i * wl.block, (i + 1) * wl.block)
+        oracle.attend_block(Q[s], K, V, idx[n], wl.block, 1.0 / math.sqrt(wl.d))
+    dt = time.perf_counter() - t0
+    flops = 4.0 * n_blocks_sample * wl.block * (topk * wl.block) * wl.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"head 0 of {wl.B * wl.H}: pool of all {wl.n_blocks} blocks of Q and K, scores+top-{topk} "
+                      f"and float64 attention for {n_blocks_sample} of {wl.n_blocks} query blocks"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the sparse-attention path has no "
+              f"multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_sparse_attention_attn_amd import sol_attn as S
+    from block_sparse_attention_attn_amd import workloads as W
+
+    S.load_library()
+    wl = W.get(args.workload)
+    topk = args.topk or wl.topk
+    t_gen = time.perf_counter()
+    q, k, v = W.make_qkv(wl)
+    t_gen = time.perf_counter() - t_gen
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if wl.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    Q, K, V = dev(q), dev(k), dev(v)
+    nb = wl.n_blocks
+    qp = torch.empty((wl.B, wl.H, nb, wl.d), dtype=torch.float64, device="cuda")
+    kp = torch.empty_like(qp)
+    idx = torch.empty((wl.B, wl.H, nb, topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(Q)
+    stream = torch.cuda.current_stream()
+    lib = S.load_library()
+    dtc = 0 if wl.dtype == "bf16" else 1
+    s_ptr = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        S._check("pool", lib.sol_attn_pool(Q.data_ptr(), K.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d, wl.block,
+                                           qp.data_ptr(), kp.data_ptr(), s_ptr))
+        if ev is not None:
+            ev[1].record(stream)
+        S._check("select", lib.sol_attn_select(qp.data_ptr(), kp.data_ptr(), wl.B, wl.H, nb, wl.d, topk,
+                                               idx.data_ptr(), None, s_ptr))
+        if ev is not None:
+            ev[2].record(stream)
+        S._check("fwd", lib.sol_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d,
+                                         wl.block, topk, idx.data_ptr(), 0.0, out.data_ptr(), None, s_ptr))
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, bracketed by synchronisation
+    t0 = time.perf_counter()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # per-kernel durations (separate pass, events between the three launches)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t_pool = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_fwd = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    flops = wl.effective_flops(topk)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = flops / (t_fwd * 1e-3) / 1e12
+    pool_bytes = 2 * wl.B * wl.H * wl.L * wl.d * (2 if wl.dtype == "bf16" else 4) + 2 * wl.B * wl.H * nb * wl.d * 8
+    rec = {
+        "metric": "sparse-attn fwd effective TFLOP/s @64.5k tokens; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded smooth field + noise, unit RMS)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d, "block": wl.block,
+                   "topk": topk, "n_blocks": nb, "latent": [wl.frames, wl.lat_h, wl.lat_w]},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"pool": round(t_pool, 4), "select": round(t_sel, 4), "fwd": round(t_fwd, 4)},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "pool_gbs": round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": FWD_TRAFFIC_BYTES if (wl.name == "refine_1344x768" and topk == wl.topk) else None},
+        "timed_wall_s": round(wall, 3),
+        "input_gen_s": round(t_gen, 2),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_sample_blocks)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,338 @@
+// Block-sparse exact softmax attention on gfx950 matrix cores (bf16 in, fp32 accumulate).
+//
+// The attention half of Sol-Attn: every query row of block i attends, with exact
+// softmax, to the tokens of the key blocks selected for block i ("Videomodel
+// MiniMax-H3 rendert sneller dan afspelen", section "Waar de snelheidswinst
+// vandaan komt").  d = 128 and 128-token blocks.
+//
+// Work unit: one workgroup = one query block (128 rows) of one (b,h); 8 waves
+// (two per SIMD).  Wave w owns query rows 32*(w%4)..+31 and key half kh = w/4
+// (keys 64*kh..64*kh+63 of every tile).  Each wave keeps its own running max,
+// sum and O over its key half; the two halves are merged once at the end
+// (exact: O = sum_h 2^(m_h-m) O_h / sum_h 2^(m_h-m) l_h).  Every unit processes
+// exactly topk key tiles, so units are equally expensive.
+//
+// Per key tile j (128 keys x 128 dims, K and V), per wave:
+//   S^T = K_j Q^T      16 MFMA 32x32x16: A = K rows from LDS (16-byte reads),
+//                      B = Q^T held in registers for the whole unit.  Computing
+//                      S transposed puts the keys of one query in the registers
+//                      of one lane pair (l, l^32), so the row max is an
+//                      in-register reduction plus one cross-half exchange.
+//   online softmax     in the log2 domain: t = s*scale*log2(e), m = running max,
+//                      p = 2^(t-m) (v_exp_f32), l += sum p, O *= 2^(m_old-m)
+//                      (skipped when no running max of the wave moved).
+//   O^T += V_j^T P^T   16 MFMA 32x32x16: the S^T accumulator layout already is
+//                      the B-operand layout of P^T (after bf16 rounding) for a
+//                      fixed permutation of the 16 keys of each k-step; the A
+//                      operand V^T is read with ds_read_b64_tr_b16, whose
+//                      16-lane transpose delivers 4 consecutive keys of one
+//                      column per lane, in the same key permutation.
+//
+// Pipelining: K and V tiles are double-buffered in LDS (4 x 32 KiB).  At the top
+// of iteration t the direct-to-LDS copies of K_{t+2} and V_{t+1} are issued into
+// the buffers freed by iteration t-1; the barrier closing iteration t waits for
+// them.  S for tile t+1 is computed in the same iteration as the softmax and PV
+// of tile t.  The two key-half waves that
+// share a SIMD run the S product and the softmax in opposite order, so one
+// wave's softmax (VALU, exp) overlaps the other's matrix-core work.
+//
+// LDS layout of a 128x128 bf16 tile: row r = 256 bytes = 16 chunks of 16 bytes;
+// logical chunk c lives at physical chunk c ^ swz(r), swz(r) = 4*(r%4) + (r/4)%4.
+// This makes both the 16-lane groups of 16-byte K reads (16 consecutive rows,
+// same chunk) and the 32-lane groups of 8-byte transpose reads (4 consecutive
+// rows x 4 consecutive chunks) hit distinct banks.
+//
+// Work order: workgroups are dispatched to the 8 XCDs round-robin; workgroup w
+// runs on XCD w%8, and XCD x is given a contiguous range of query blocks of the
+// same head as every other XCD at that moment.  All XCDs thus stream the same
+// head's K/V (kept in the shared last-level cache), while each XCD's L2 serves
+// the overlapping selections of its neighbouring query blocks.
+#include "launchers.h"
+
+namespace sol_attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 128;
+constexpr int kD = 128;
+constexpr int kThreads = 512;
+constexpr int kTileBytes = kBlock * kD * 2;   // 32 KiB
+constexpr int kLds = 4 * kTileBytes;          // K0 K1 V0 V1
+constexpr int kXcds = 8;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ i16x4 ds_read_tr(const unsigned char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)(base) + off));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Global -> LDS tile copy with the gfx950 direct-to-LDS load (no register staging).
+// One wave instruction writes 64 lanes x 16 bytes = 1 KiB of LDS contiguously
+// (= 4 tile rows).  Lane l of segment s fills physical chunk l%16 of row
+// 4s + l/16, so it fetches the logical chunk that the swizzle places there; the
+// 16 lanes of a row still read that row's 256 contiguous bytes.  Wave w copies
+// segments w, w+8, w+16, w+24.  Completion is awaited by the next barrier.
+__device__ __forceinline__ void tile_dma(unsigned char* lds, const unsigned char* __restrict__ g,
+                                         int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int seg = wave + 8 * i;
+    const int row = 4 * seg + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    __builtin_amdgcn_global_load_lds(
+        static_cast<const void*>(g + (size_t)row * 256 + c * 16),
+        (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16, 0, 0);
+  }
+}
+
+// S^T (64 keys of this wave's half x 32 queries) = K_half . Q^T.
+__device__ __forceinline__ void compute_st(f32x16 (&s)[2], const unsigned char* kt, int key0,
+                                           const bf16x8 (&qf)[8], int n, int h) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    s[mb] = f32x16{};
+    const int row = key0 + 32 * mb + n;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + lds_off(row, 2 * ks + h));
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+    }
+  }
+  // keep at most two operand reads ahead of the matrix core (bounds register use)
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
+    const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
+    const unsigned char* __restrict__ v, const int32_t* __restrict__ block_idx, int BH, int L,
+    int n_blocks, int topk, int per_xcd, float scale_log2, unsigned char* __restrict__ out,
+    float* __restrict__ lse) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* kbuf[2] = {smem, smem + kTileBytes};
+  unsigned char* vbuf[2] = {smem + 2 * kTileBytes, smem + 3 * kTileBytes};
+
+  // ---- work mapping (XCD-aware, head-major across the whole chip)
+  const int wg = blockIdx.x;
+  const int xcd = wg % kXcds;
+  const int slot = wg / kXcds;
+  const int bh = slot / per_xcd;
+  const int qb = xcd * per_xcd + slot % per_xcd;
+  if (bh >= BH || qb >= n_blocks) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int qg = wave & 3;     // query group: rows 32*qg..+31 of the block
+  const int kh = wave >> 2;    // key half: keys 64*kh..+63 of every tile
+  const int n = lane & 31;     // query within the group (MFMA column)
+  const int h = lane >> 5;     // lane half
+  const int key0 = 64 * kh;
+
+  const size_t head_off = (size_t)bh * L * kD * 2;    // bytes
+  const unsigned char* kh_ptr = k + head_off;
+  const unsigned char* vh_ptr = v + head_off;
+  const int32_t* sel = block_idx + ((size_t)bh * n_blocks + qb) * topk;
+  auto tile_src = [&](const unsigned char* base, int t) {
+    const int j = min(max(sel[t], 0), n_blocks - 1);
+    return base + (size_t)j * kTileBytes;
+  };
+
+  // ---- Q^T operand: lane holds Q[query n][16*ks + 8*h + 0..7] for ks = 0..7
+  const int qrow = qb * kBlock + qg * 32 + n;
+  bf16x8 qf[8];
+  {
+    const unsigned char* qp = q + head_off + (size_t)qrow * kD * 2;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (16 * ks + 8 * h) * 2);
+  }
+
+  // ---- transpose-read addressing for V^T operands (per lane, loop invariant)
+  // group g = lane/16 covers keys 4*(g/2)+0..3 (rows) x dims 16*(g%2)+0..15 of a 32-dim block.
+  const int g = lane >> 4;
+  const int rr = (lane & 15) >> 2, cc = lane & 3;
+  const int tr_row0 = key0 + 4 * (g >> 1) + rr;                  // + 16*ks (+8)
+  const int tr_col = 16 * (g & 1) + 4 * cc;                      // + 32*md   (elements)
+  // Rows 16*ks + tr_row0 (+8) have the same swizzle for every ks (16*ks changes
+  // neither row%4 nor (row/4)%4), so each (md, lo/hi) needs one base offset and
+  // the k-step becomes an immediate offset of 16 rows * 256 bytes.
+  int tr_off[2][4];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {
+      const int row = tr_row0 + 8 * hi;
+      const int col = 32 * md + tr_col;
+      tr_off[hi][md] = row * 256 + (((col >> 3) ^ swz(row)) << 4) + (col & 7) * 2;
+    }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int md = 0; md < 4; ++md) o[md] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- prologue: K0, V0, K1 into LDS; S_0
+  tile_dma(kbuf[0], tile_src(kh_ptr, 0), wave, lane);
+  tile_dma(vbuf[0], tile_src(vh_ptr, 0), wave, lane);
+  if (topk > 1) tile_dma(kbuf[1], tile_src(kh_ptr, 1), wave, lane);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  compute_st(sa, kbuf[0], key0, qf, n, h);
+  __syncthreads();   // every wave is done with K0 before iteration 0 refills its buffer
+
+  auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int t, int par) {
+    const bool has_next = t + 1 < topk;
+    // refill the buffers freed by the previous iteration: K_{t+2} and V_{t+1}
+    if (t + 2 < topk) tile_dma(kbuf[par], tile_src(kh_ptr, t + 2), wave, lane);
+    if (has_next) tile_dma(vbuf[par ^ 1], tile_src(vh_ptr, t + 1), wave, lane);
+    // key half 0 computes the next S first, key half 1 after its softmax
+    if (kh == 0 && has_next) compute_st(snext, kbuf[par ^ 1], key0, qf, n, h);
+
+    // softmax on S_t (log2 domain)
+    float mx = scur[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[mb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+    uint32_t pb[4][4];   // P^T operand per k-step (8 bf16 = 4 dwords)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r], scale_log2, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r + 1], scale_log2, -m_new));
+        lsum += p0 + p1;
+        // register r of block mb holds key key0 + 32mb + 8(r/4) + 4h + r%4;
+        // k-step ks = 2mb + r/8 takes r/4 even -> dwords 0,1 ; odd -> dwords 2,3
+        const int ks = 2 * mb + (r >> 3);
+        const int dw = ((r >> 2) & 1) * 2 + ((r & 3) >> 1);
+        pb[ks][dw] = pack_bf16x2(p0, p1);
+      }
+    }
+    l_run = l_run * alpha + lsum;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+    }
+
+    if (kh == 1 && has_next) compute_st(snext, kbuf[par ^ 1], key0, qf, n, h);
+
+    // O^T += V^T P^T over this wave's 64 keys
+    const unsigned char* vt = vbuf[par];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]});
+      const unsigned char* vk = vt + ks * 16 * 256;
+#pragma unroll
+      for (int md = 0; md < 4; ++md) {
+        const i16x4 lo = ds_read_tr(vk, tr_off[0][md]);
+        const i16x4 hi = ds_read_tr(vk, tr_off[1][md]);
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[md], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+
+    __syncthreads();   // also waits for this iteration's tile copies
+  };
+
+  int t = 0;
+  for (; t + 1 < topk; t += 2) {
+    step(sa, sb, t, 0);
+    step(sb, sa, t + 1, 1);
+  }
+  if (t < topk) step(sa, sb, t, 0);
+
+  // ---- merge the two key halves: half 1 publishes (m, l, O^T) through LDS (tile buffers are free)
+  float* xch = reinterpret_cast<float*>(smem);        // [qg][66][64 lanes]
+  float* mine = xch + qg * 66 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[(md * 16 + r) * 64 + lane] = o[md][r];
+    mine[64 * 64 + lane] = m_run;
+    mine[65 * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = mine[64 * 64 + lane], l1 = mine[65 * 64 + lane];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+  const float l_lane = l_run * a0 + l1 * a1;
+  const float l_tot = l_lane + __shfl_xor(l_lane, 32, 64);
+  const float inv = 1.f / l_tot;
+  const float c0 = a0 * inv, c1 = a1 * inv;
+  unsigned char* op = out + head_off + (size_t)qrow * kD * 2;
+#pragma unroll
+  for (int md = 0; md < 4; ++md)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // registers 4j..4j+3 hold dims 32md + 8j + 4h + 0..3 of query n
+      const int dcol = 32 * md + 8 * j + 4 * h;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = o[md][4 * j + i] * c0 + mine[(md * 16 + 4 * j + i) * 64 + lane] * c1;
+      u32x2 w{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(op + dcol * 2) = w;
+    }
+  if (lse && h == 0) lse[(size_t)bh * L + qrow] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, int L, int topk,
+                           const int32_t* block_idx, float scale, void* out, float* lse,
+                           hipStream_t stream) {
+  const int n_blocks = L / kBlock;
+  const int per_xcd = (n_blocks + kXcds - 1) / kXcds;
+  const long long grid = (long long)kXcds * per_xcd * BH;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (err != hipSuccess) return err;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(fwd_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), kLds, stream,
+                     static_cast<const unsigned char*>(q), static_cast<const unsigned char*>(k),
+                     static_cast<const unsigned char*>(v), block_idx, BH, L, n_blocks, topk, per_xcd,
+                     scale_log2, static_cast<unsigned char*>(out), lse);
+  return hipGetLastError();
+}
+
+}  // namespace sol_attn

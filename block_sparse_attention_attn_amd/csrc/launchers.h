@@ -1,0 +1,26 @@
+// Kernel launchers behind the C ABI (internal; argument checking happens in sol_attn_api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sol_attn {
+
+// Block mean-pooling of q and k.  is_bf16 selects the element type.
+hipError_t launch_pool(const void* q, const void* k, bool is_bf16, int BH, int L, int d, int block,
+                       double* q_pooled, double* k_pooled, hipStream_t stream);
+
+// Top-k key-block selection by pooled score.
+hipError_t launch_select(const double* q_pooled, const double* k_pooled, int BH, int n_blocks, int d,
+                         int topk, int32_t* block_idx, double* scores_or_null, hipStream_t stream);
+
+// Sparse attention, bf16 matrix-core path (d == block == 128).
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, int L, int topk,
+                           const int32_t* block_idx, float scale, void* out, float* lse,
+                           hipStream_t stream);
+
+// Sparse attention, fp32 path (d in {64,128}, block <= 256).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH, int L, int d,
+                          int block, int topk, const int32_t* block_idx, float scale, float* out,
+                          float* lse, hipStream_t stream);
+
+}  // namespace sol_attn

@@ -1,0 +1,131 @@
+// C ABI of the Sol-Attn library: argument checking, dispatch, error reporting.
+// Every check runs on the host before any HIP call, so a rejected call enqueues
+// nothing and touches no output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/sol_attn.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SOL_ATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SOL_ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int dtype, int B, int H, int L, int d, int block) {
+  if (dtype != SOL_ATTN_BF16 && dtype != SOL_ATTN_FP32)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (B < 0 || H < 0 || L < 0) return fail(SOL_ATTN_ERR_SHAPE, "negative size B=%d H=%d L=%d", B, H, L);
+  if (d <= 0 || block <= 0) return fail(SOL_ATTN_ERR_SHAPE, "d=%d and block=%d must be positive", d, block);
+  if (L % block != 0) return fail(SOL_ATTN_ERR_SHAPE, "L=%d is not a multiple of block=%d", L, block);
+  if ((long long)B * H > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "B*H too large");
+  return SOL_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, int d, int block,
+                  double* q_pooled, double* k_pooled, void* stream) {
+  int st = check_common(dtype, B, H, L, d, block);
+  if (st != SOL_ATTN_OK) return st;
+  const bool bf16 = dtype == SOL_ATTN_BF16;
+  if (d > 512 || d % (bf16 ? 8 : 4) != 0)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "pool needs d <= 512 and d %% %d == 0 (d=%d)", bf16 ? 8 : 4, d);
+  const long long BH = (long long)B * H;
+  if (BH * L == 0) return ok();
+  if (L / block > 0x7fffffff || BH > 65535)
+    return fail(SOL_ATTN_ERR_SHAPE, "pool grid too large (B*H must be <= 65535)");
+  if (!q || !k || !q_pooled || !k_pooled) return fail(SOL_ATTN_ERR_NULL, "pool: NULL pointer");
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(SOL_ATTN_ERR_ALIGN, "pool: q/k not 16-byte aligned");
+  if (!aligned(q_pooled, 8) || !aligned(k_pooled, 8))
+    return fail(SOL_ATTN_ERR_ALIGN, "pool: pooled outputs not 8-byte aligned");
+  return hip_status(sol_attn::launch_pool(q, k, bf16, (int)BH, L, d, block, q_pooled, k_pooled,
+                                          static_cast<hipStream_t>(stream)),
+                    "pool launch");
+}
+
+int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,
+                    int topk, int32_t* block_idx, double* scores_or_null, void* stream) {
+  if (B < 0 || H < 0 || n_blocks < 0) return fail(SOL_ATTN_ERR_SHAPE, "negative size");
+  if (d <= 0) return fail(SOL_ATTN_ERR_SHAPE, "d=%d must be positive", d);
+  if (d > 512) return fail(SOL_ATTN_ERR_UNSUPPORTED, "select needs d <= 512 (d=%d)", d);
+  if (n_blocks > 16384) return fail(SOL_ATTN_ERR_UNSUPPORTED, "select needs n_blocks <= 16384");
+  const long long BH = (long long)B * H;
+  if (BH * n_blocks == 0) return ok();
+  if (topk < 1 || topk > n_blocks)
+    return fail(SOL_ATTN_ERR_K, "topk=%d outside [1, n_blocks=%d]", topk, n_blocks);
+  if (BH > 65535) return fail(SOL_ATTN_ERR_SHAPE, "select grid too large (B*H must be <= 65535)");
+  if (!q_pooled || !k_pooled || !block_idx) return fail(SOL_ATTN_ERR_NULL, "select: NULL pointer");
+  if (!aligned(q_pooled, 8) || !aligned(k_pooled, 8) || !aligned(block_idx, 4) ||
+      (scores_or_null && !aligned(scores_or_null, 8)))
+    return fail(SOL_ATTN_ERR_ALIGN, "select: misaligned pointer");
+  return hip_status(sol_attn::launch_select(q_pooled, k_pooled, (int)BH, n_blocks, d, topk, block_idx,
+                                            scores_or_null, static_cast<hipStream_t>(stream)),
+                    "select launch");
+}
+
+int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
+                 int block, int topk, const int32_t* block_idx, float softmax_scale, void* out,
+                 float* lse_or_null, void* stream) {
+  int st = check_common(dtype, B, H, L, d, block);
+  if (st != SOL_ATTN_OK) return st;
+  const bool bf16 = dtype == SOL_ATTN_BF16;
+  if (bf16 && !(d == 128 && block == 128))
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "bf16 fwd needs d == 128 and block == 128 (d=%d block=%d)", d, block);
+  if (!bf16 && !((d == 64 || d == 128) && block <= 256))
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "fp32 fwd needs d in {64,128} and block <= 256 (d=%d block=%d)", d,
+                block);
+  const long long BH = (long long)B * H;
+  if (BH * L == 0) return ok();
+  const int n_blocks = L / block;
+  if (topk < 1 || topk > n_blocks) return fail(SOL_ATTN_ERR_K, "topk=%d outside [1, n_blocks=%d]", topk, n_blocks);
+  if (!bf16 && BH > 65535) return fail(SOL_ATTN_ERR_SHAPE, "fp32 fwd grid too large (B*H must be <= 65535)");
+  if (!q || !k || !v || !block_idx || !out) return fail(SOL_ATTN_ERR_NULL, "fwd: NULL pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(SOL_ATTN_ERR_ALIGN, "fwd: q/k/v/out not 16-byte aligned");
+  if (!aligned(block_idx, 4) || (lse_or_null && !aligned(lse_or_null, 4)))
+    return fail(SOL_ATTN_ERR_ALIGN, "fwd: block_idx/lse not 4-byte aligned");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bf16)
+    return hip_status(sol_attn::launch_fwd_bf16(q, k, v, (int)BH, L, topk, block_idx, scale, out,
+                                                lse_or_null, s),
+                      "fwd bf16 launch");
+  return hip_status(sol_attn::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                             static_cast<const float*>(v), (int)BH, L, d, block, topk,
+                                             block_idx, scale, static_cast<float*>(out), lse_or_null, s),
+                    "fwd fp32 launch");
+}
+
+const char* sol_attn_last_error(void) { return g_last_error.c_str(); }
+
+int sol_attn_version(void) { return SOL_ATTN_VERSION; }
+
+}  // extern "C"

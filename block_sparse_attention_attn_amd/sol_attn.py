@@ -1,0 +1,159 @@
+"""Thin ctypes binding of libsol_attn.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks torch tensors, allocates outputs with torch on the inputs' device and
+passes raw device pointers plus the current HIP stream.  It never falls back to
+another implementation: if the library is missing, calls raise.
+
+Calls (same names as the C ABI):
+  sol_attn_pool(q, k, block)                         -> (q_pooled, k_pooled) float64 [B,H,L/block,d]
+  sol_attn_select(q_pooled, k_pooled, topk, ...)     -> block_idx int32 [B,H,nB,topk] (+ scores)
+  sol_attn_fwd(q, k, v, block_idx, block, ...)       -> out [B,H,L,d] (+ lse float32 [B,H,L])
+  sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsol_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "sol_attn.h")
+
+BF16, FP32 = 0, 1
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_K", 4: "ERR_UNSUPPORTED", 5: "ERR_ALIGN", 6: "ERR_HIP"}
+
+_lib = None
+
+
+class SolAttnError(RuntimeError):
+    def __init__(self, call: str, code: int, msg: str):
+        super().__init__(f"{call} failed with {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m block_sparse_attention_attn_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    lib.sol_attn_pool.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, vp]
+    lib.sol_attn_pool.restype = i
+    lib.sol_attn_select.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
+    lib.sol_attn_select.restype = i
+    lib.sol_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, ctypes.c_float, vp, vp, vp]
+    lib.sol_attn_fwd.restype = i
+    lib.sol_attn_last_error.argtypes = []
+    lib.sol_attn_last_error.restype = ctypes.c_char_p
+    lib.sol_attn_version.argtypes = []
+    lib.sol_attn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def header_symbols(path: str = HEADER_PATH):
+    """Names of the functions the public header declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sol_attn_\w+)\s*\(", text)))
+
+
+def _check(call: str, code: int):
+    if code != 0:
+        raise SolAttnError(call, code, _lib.sol_attn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_qkv(*ts: torch.Tensor):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, L, d]")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def sol_attn_pool(q: torch.Tensor, k: torch.Tensor, block: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    lib = load_library()
+    _check_qkv(q, k)
+    B, H, L, d = q.shape
+    nb = L // block if block > 0 else 0
+    qp = torch.empty((B, H, nb, d), dtype=torch.float64, device=q.device)
+    kp = torch.empty_like(qp)
+    _check("sol_attn_pool", lib.sol_attn_pool(_ptr(q), _ptr(k), _dtype_code(q), B, H, L, d, block,
+                                              _ptr(qp), _ptr(kp), _stream(q)))
+    return qp, kp
+
+
+def sol_attn_select(q_pooled: torch.Tensor, k_pooled: torch.Tensor, topk: int, return_scores: bool = False):
+    lib = load_library()
+    if q_pooled.dtype != torch.float64 or k_pooled.dtype != torch.float64:
+        raise TypeError("pooled tensors must be float64")
+    if q_pooled.shape != k_pooled.shape or not (q_pooled.is_contiguous() and k_pooled.is_contiguous()):
+        raise ValueError("pooled tensors must be contiguous [B,H,nB,d] of equal shape")
+    B, H, nb, d = q_pooled.shape
+    idx = torch.empty((B, H, nb, max(topk, 0)), dtype=torch.int32, device=q_pooled.device)
+    scores = torch.empty((B, H, nb, nb), dtype=torch.float64, device=q_pooled.device) if return_scores else None
+    _check("sol_attn_select", lib.sol_attn_select(_ptr(q_pooled), _ptr(k_pooled), B, H, nb, d, topk, _ptr(idx),
+                                                  _ptr(scores), _stream(q_pooled)))
+    return (idx, scores) if return_scores else idx
+
+
+def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor, block: int,
+                 softmax_scale: Optional[float] = None, return_lse: bool = False,
+                 out: Optional[torch.Tensor] = None):
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, L, d = q.shape
+    if block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4:
+        raise ValueError("block_idx must be contiguous int32 [B,H,nB,topk]")
+    topk = block_idx.shape[-1]
+    if block > 0 and tuple(block_idx.shape[:3]) != (B, H, L // block):
+        raise ValueError("block_idx leading dims must be [B,H,L/block]")
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check("sol_attn_fwd", lib.sol_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, L, d, block, topk,
+                                            _ptr(block_idx), scale, _ptr(out), _ptr(lse), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
+                     softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """Pool -> select -> fwd.  Returns out (and lse), plus nothing else; use the
+    individual calls to inspect the pooled tensors or the selected blocks."""
+    qp, kp = sol_attn_pool(q, k, block)
+    idx = sol_attn_select(qp, kp, topk)
+    return sol_attn_fwd(q, k, v, idx, block, softmax_scale, return_lse)
+
+
+def version() -> int:
+    return load_library().sol_attn_version()

@@ -1,0 +1,122 @@
+/*
+ * sol_attn.h -- C ABI of the Sol-Attn block-sparse attention library for MI355X (gfx950).
+ *
+ * What is computed.  Sol-Attn is the training-free sparse attention of the Sol-H3
+ * runtime: for every query it decides which parts of the attention computation
+ * matter, and it is the largest single source of that runtime's speed-up; its
+ * preparation step (the selection that precedes the attention) was itself
+ * optimised ("Videomodel MiniMax-H3 rendert sneller dan afspelen", section
+ * "Waar de snelheidswinst vandaan komt").  It runs in the high-resolution
+ * refinement steps of the two-stage schedule ("NVIDIA Adds Two-Stage Generation
+ * for MiniMax H3, ...", first paragraph).  The pages give no formula; this
+ * library implements the following concrete reading, in three calls:
+ *
+ *   sol_attn_pool    Qbar_i = mean of the Bs query rows of block i, Kbar_j likewise
+ *                    (tokens are frame-major; block i = tokens [i*Bs, (i+1)*Bs)).
+ *   sol_attn_select  r_ij = Qbar_i . Kbar_j; per query block i keep the `topk` key
+ *                    blocks j with the largest r_ij, ties to the lower j (the score
+ *                    r_ij/sqrt(d) has the same order); emit them in ascending j.
+ *   sol_attn_fwd     every query row of block i attends with exact
+ *                    softmax(q k^T * scale) over the tokens of its selected key
+ *                    blocks only; no mask.
+ *
+ * Layout.  Q, K, V and O are contiguous [B, H, L, d] row-major (d fastest), in the
+ * element type given by `dtype`.  Pooled tensors are [B, H, L/block, d] float64.
+ * The block index list is int32 [B, H, L/block, topk], ascending per row.
+ *
+ * Ownership and execution.  Every pointer argument is a DEVICE pointer owned by
+ * the caller; the library allocates no memory, keeps no state between calls and
+ * never retains a pointer.  Calls enqueue their kernel(s) on `stream` (a
+ * hipStream_t; NULL = the default stream) and return without synchronising;
+ * results are valid once the stream has reached that point.  Outputs must not
+ * alias inputs.  Calls are thread-safe.
+ *
+ * Errors.  Argument errors are detected on the host before anything is enqueued
+ * and leave every output untouched.  A failure reported by the HIP runtime at
+ * launch returns SOL_ATTN_ERR_HIP.  sol_attn_last_error() describes the most
+ * recent failure on the calling thread.  Faults inside a kernel surface at the
+ * caller's next synchronisation, as for any HIP library.  Problems with zero
+ * elements (B*H*L == 0) are valid and enqueue nothing.
+ */
+#ifndef SOL_ATTN_H_
+#define SOL_ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SOL_ATTN_VERSION 100  /* major*100 + minor */
+
+typedef enum {
+  SOL_ATTN_BF16 = 0,  /* bfloat16 inputs/outputs, float32 accumulation */
+  SOL_ATTN_FP32 = 1   /* float32 inputs/outputs, float32 arithmetic */
+} sol_attn_dtype_t;
+
+typedef enum {
+  SOL_ATTN_OK = 0,
+  SOL_ATTN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  SOL_ATTN_ERR_SHAPE = 2,       /* negative size, d/block <= 0, or L % block != 0      */
+  SOL_ATTN_ERR_K = 3,           /* topk < 1 or topk > L/block                          */
+  SOL_ATTN_ERR_UNSUPPORTED = 4, /* dtype / d / block combination not built (see calls) */
+  SOL_ATTN_ERR_ALIGN = 5,       /* pointer not aligned as the call requires            */
+  SOL_ATTN_ERR_HIP = 6          /* the HIP runtime rejected a launch                   */
+} sol_attn_status_t;
+
+/*
+ * Block mean-pooling of Q and K (the first half of the selection "preparation").
+ *   q, k        [B,H,L,d] of `dtype`; 16-byte aligned.
+ *   q_pooled,   [B,H,L/block,d] float64 outputs; 8-byte aligned.
+ *   k_pooled    Element (b,h,i,e) = (sum over the block's rows of x[b,h,i*block+t,e]) / block.
+ *               The block sum is accumulated in float64 (exact whenever the block's
+ *               values span less than ~2^35 in magnitude, so then order-independent);
+ *               the division is IEEE-correctly rounded.
+ * Supported: dtype BF16 with d % 8 == 0, or FP32 with d % 4 == 0; d <= 512; any block >= 1.
+ */
+int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, int d, int block,
+                  double* q_pooled, double* k_pooled, void* stream);
+
+/*
+ * Top-k key-block selection per query block (the second half of the preparation).
+ *   q_pooled, k_pooled  [B,H,n_blocks,d] float64 (as written by sol_attn_pool); 8-byte aligned.
+ *   block_idx           int32 [B,H,n_blocks,topk] output, ascending per row; 4-byte aligned.
+ *                       Row (b,h,i) holds the first `topk` key blocks j in the order
+ *                       (r_ij descending, j ascending), r_ij = sum_e Qbar_ie*Kbar_je in float64.
+ *   scores_or_null      optional float64 [B,H,n_blocks,n_blocks] output of r_ij/sqrt(d).
+ * Supported: 1 <= d <= 512, n_blocks <= 16384, 1 <= topk <= n_blocks.  -0.0 and +0.0 rank as equal.
+ * Rows whose scores contain NaN get an unspecified (but in-range) selection.
+ */
+int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,
+                    int topk, int32_t* block_idx, double* scores_or_null, void* stream);
+
+/*
+ * Block-sparse exact softmax attention over the selected key blocks.
+ *   q, k, v        [B,H,L,d] of `dtype`; 16-byte aligned.
+ *   block_idx      int32 [B,H,L/block,topk]; every entry must lie in [0, L/block) and the
+ *                  entries of a row must be distinct (sol_attn_select guarantees both).
+ *                  Out-of-range entries are clamped into range instead of faulting; the
+ *                  affected rows' results are then unspecified.
+ *   softmax_scale  multiplier of q.k inside the softmax; <= 0 selects 1/sqrt(d).
+ *   out            [B,H,L,d] of `dtype`: O = softmax(q K_sel^T * scale) V_sel per query row;
+ *                  bf16 results are rounded to nearest-even from float32.
+ *   lse_or_null    optional float32 [B,H,L]: natural-log log-sum-exp of the scaled logits.
+ * Supported: BF16 with d == 128 and block == 128 (matrix-core path, float32 accumulation;
+ * probabilities are rounded to bf16 before the P.V product), or FP32 with d in {64,128}
+ * and 1 <= block <= 256.  16-byte alignment for q,k,v,out; 4-byte for lse and block_idx.
+ */
+int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
+                 int block, int topk, const int32_t* block_idx, float softmax_scale, void* out,
+                 float* lse_or_null, void* stream);
+
+/* Human-readable description of the last failure on the calling thread ("" if none). */
+const char* sol_attn_last_error(void);
+
+/* SOL_ATTN_VERSION of the built library. */
+int sol_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOL_ATTN_H_ */

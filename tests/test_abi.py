@@ -1,0 +1,104 @@
+"""The C-ABI library loads on the host and exports what include/sol_attn.h declares, and
+its argument checks reject bad calls before anything touches a GPU (no compute calls
+here: every call below returns from host-side validation)."""
+import ctypes
+import os
+
+import pytest
+
+from block_sparse_attention_attn_amd import sol_attn as S
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(S.LIB_PATH):
+        from block_sparse_attention_attn_amd import build
+        build.build()
+    return S.load_library()
+
+
+def test_header_symbols_exported(lib):
+    names = S.header_symbols()
+    assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
+                          "sol_attn_version"}
+    raw = ctypes.CDLL(S.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version(lib):
+    assert lib.sol_attn_version() == 100
+
+
+FAKE = 0x10000      # 64 KiB-aligned dummy "device" address; never dereferenced
+MIS = FAKE + 2      # misaligned
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, H=1, L=256, d=128, block=128, topk=1, idx=FAKE,
+         out=FAKE, lse=None):
+    return lib.sol_attn_fwd(q, k, v, dtype, B, H, L, d, block, topk, idx, 0.0, out, lse, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert _fwd(lib, dtype=7) == 4
+    assert _fwd(lib, B=-1) == 2
+    assert _fwd(lib, L=200) == 2                       # not a multiple of block
+    assert _fwd(lib, block=0) == 2
+    assert _fwd(lib, d=64) == 4                        # bf16 path needs d = block = 128
+    assert _fwd(lib, block=64, L=256) == 4
+    assert _fwd(lib, dtype=1, d=96, block=64) == 4     # fp32 needs d in {64,128}
+    assert _fwd(lib, dtype=1, d=64, block=512, L=1024) == 4
+    assert _fwd(lib, topk=0) == 3
+    assert _fwd(lib, topk=3) == 3                      # only 2 blocks
+    assert _fwd(lib, q=None) == 1
+    assert _fwd(lib, idx=None) == 1
+    assert _fwd(lib, out=None) == 1
+    assert _fwd(lib, v=MIS) == 5
+    assert _fwd(lib, lse=FAKE + 2) == 5
+    assert b"topk" in lib.sol_attn_last_error() or b"aligned" in lib.sol_attn_last_error()
+
+
+def test_fwd_empty_problem_is_a_noop(lib):
+    # zero-element problems are valid and enqueue nothing (no GPU needed)
+    assert _fwd(lib, B=0, q=None, k=None, v=None, idx=None, out=None) == 0
+    assert _fwd(lib, H=0, topk=99) == 0
+    assert _fwd(lib, L=0) == 0
+    assert lib.sol_attn_last_error() == b""
+
+
+def test_pool_argument_errors(lib):
+    p = lambda **kw: lib.sol_attn_pool(kw.get("q", FAKE), kw.get("k", FAKE), kw.get("dtype", 0), kw.get("B", 1),  # noqa: E731
+                                       kw.get("H", 1), kw.get("L", 256), kw.get("d", 128), kw.get("block", 128),
+                                       kw.get("qp", FAKE), kw.get("kp", FAKE), None)
+    assert p(dtype=3) == 4
+    assert p(L=100) == 2
+    assert p(d=12) == 4          # bf16 pool needs d % 8 == 0
+    assert p(d=1024) == 4
+    assert p(q=None) == 1
+    assert p(kp=None) == 1
+    assert p(k=MIS) == 5
+    assert p(qp=FAKE + 4) == 5
+    assert p(B=0, q=None) == 0
+
+
+def test_select_argument_errors(lib):
+    s = lambda **kw: lib.sol_attn_select(kw.get("qp", FAKE), kw.get("kp", FAKE), kw.get("B", 1), kw.get("H", 1),  # noqa: E731
+                                         kw.get("nb", 8), kw.get("d", 128), kw.get("topk", 2), kw.get("idx", FAKE),
+                                         kw.get("scores", None), None)
+    assert s(topk=0) == 3
+    assert s(topk=9) == 3
+    assert s(nb=-1) == 2
+    assert s(d=0) == 2
+    assert s(d=1000) == 4
+    assert s(nb=20000, topk=1) == 4
+    assert s(idx=None) == 1
+    assert s(idx=FAKE + 2) == 5
+    assert s(scores=FAKE + 4) == 5
+    assert s(nb=0, topk=0) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.sol_attn_pool(q, q, 128)
