@@ -104,6 +104,8 @@ def main():
     kp = torch.empty_like(qp)
     idx = torch.empty((wl.B, wl.H, nb, topk), dtype=torch.int32, device="cuda")
     out = torch.empty_like(Q)
+    # schedule query blocks covering the same latent rows of all frames together (cache reuse)
+    order = S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w).cuda()
     stream = torch.cuda.current_stream()
     lib = S.load_library()
     dtc = 0 if wl.dtype == "bf16" else 1
@@ -121,7 +123,8 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         S._check("fwd", lib.sol_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d,
-                                         wl.block, topk, idx.data_ptr(), 0.0, out.data_ptr(), None, s_ptr))
+                                         wl.block, topk, idx.data_ptr(), order.data_ptr(), 0.0, out.data_ptr(),
+                                         None, s_ptr))
         if ev is not None:
             ev[3].record(stream)
 

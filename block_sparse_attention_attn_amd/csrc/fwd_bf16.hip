@@ -62,7 +62,6 @@ constexpr int kBlock = 128;
 constexpr int kD = 128;
 constexpr int kThreads = 512;
 constexpr int kTileBytes = kBlock * kD * 2;   // 32 KiB
-constexpr int kLds = 4 * kTileBytes;          // K0 K1 V0 V1
 constexpr int kXcds = 8;
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
@@ -78,9 +77,12 @@ __device__ __forceinline__ i16x4 ds_read_tr(const unsigned char* base, int off) 
       (lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)(base) + off));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even): one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Global -> LDS tile copy with the gfx950 direct-to-LDS load (no register staging).
@@ -127,20 +129,28 @@ __device__ __forceinline__ void compute_st(f32x16 (&s)[2], const unsigned char* 
 
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
-    const unsigned char* __restrict__ v, const int32_t* __restrict__ block_idx, int BH, int L,
+    const unsigned char* __restrict__ v, const int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ qblock_order, int BH, int L,
     int n_blocks, int topk, int per_xcd, float scale_log2, unsigned char* __restrict__ out,
     float* __restrict__ lse) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* kbuf[2] = {smem, smem + kTileBytes};
-  unsigned char* vbuf[2] = {smem + 2 * kTileBytes, smem + 3 * kTileBytes};
+  // Four separate LDS arrays (not one): the compiler can then prove that reads of
+  // one buffer never alias the in-flight direct-to-LDS copies into another, and
+  // does not insert a wait for those copies in the middle of the iteration.
+  __shared__ __attribute__((aligned(16))) unsigned char k0s[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char k1s[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v0s[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v1s[kTileBytes];
+  auto kbuf = [&](int p) { return p ? k1s : k0s; };
+  auto vbuf = [&](int p) { return p ? v1s : v0s; };
 
   // ---- work mapping (XCD-aware, head-major across the whole chip)
   const int wg = blockIdx.x;
   const int xcd = wg % kXcds;
   const int slot = wg / kXcds;
   const int bh = slot / per_xcd;
-  const int qb = xcd * per_xcd + slot % per_xcd;
-  if (bh >= BH || qb >= n_blocks) return;
+  const int pos = xcd * per_xcd + slot % per_xcd;
+  if (bh >= BH || pos >= n_blocks) return;
+  const int qb = qblock_order ? min(max(qblock_order[pos], 0), n_blocks - 1) : pos;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,21 +204,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   // ---- prologue: K0, V0, K1 into LDS; S_0
-  tile_dma(kbuf[0], tile_src(kh_ptr, 0), wave, lane);
-  tile_dma(vbuf[0], tile_src(vh_ptr, 0), wave, lane);
-  if (topk > 1) tile_dma(kbuf[1], tile_src(kh_ptr, 1), wave, lane);
+  tile_dma(kbuf(0), tile_src(kh_ptr, 0), wave, lane);
+  tile_dma(vbuf(0), tile_src(vh_ptr, 0), wave, lane);
+  if (topk > 1) tile_dma(kbuf(1), tile_src(kh_ptr, 1), wave, lane);
   __syncthreads();
   f32x16 sa[2], sb[2];
-  compute_st(sa, kbuf[0], key0, qf, n, h);
+  compute_st(sa, kbuf(0), key0, qf, n, h);
   __syncthreads();   // every wave is done with K0 before iteration 0 refills its buffer
 
   auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int t, int par) {
     const bool has_next = t + 1 < topk;
     // refill the buffers freed by the previous iteration: K_{t+2} and V_{t+1}
-    if (t + 2 < topk) tile_dma(kbuf[par], tile_src(kh_ptr, t + 2), wave, lane);
-    if (has_next) tile_dma(vbuf[par ^ 1], tile_src(vh_ptr, t + 1), wave, lane);
+    if (t + 2 < topk) tile_dma(kbuf(par), tile_src(kh_ptr, t + 2), wave, lane);
+    if (has_next) tile_dma(vbuf(par ^ 1), tile_src(vh_ptr, t + 1), wave, lane);
     // key half 0 computes the next S first, key half 1 after its softmax
-    if (kh == 0 && has_next) compute_st(snext, kbuf[par ^ 1], key0, qf, n, h);
+    if (kh == 0 && has_next) compute_st(snext, kbuf(par ^ 1), key0, qf, n, h);
 
     // softmax on S_t (log2 domain)
     float mx = scur[0][0];
@@ -244,10 +254,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
     }
 
-    if (kh == 1 && has_next) compute_st(snext, kbuf[par ^ 1], key0, qf, n, h);
+    if (kh == 1 && has_next) compute_st(snext, kbuf(par ^ 1), key0, qf, n, h);
 
     // O^T += V^T P^T over this wave's 64 keys
-    const unsigned char* vt = vbuf[par];
+    const unsigned char* vt = vbuf(par);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]});
@@ -280,8 +290,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   if (t < topk) step(sa, sb, t, 0);
 
   // ---- merge the two key halves: half 1 publishes (m, l, O^T) through LDS (tile buffers are free)
-  float* xch = reinterpret_cast<float*>(smem);        // [qg][66][64 lanes]
-  float* mine = xch + qg * 66 * 64;
+  // one free 32 KiB tile buffer per query group holds its [66][64 lanes] floats (16.5 KiB)
+  unsigned char* xbuf = qg == 0 ? k0s : (qg == 1 ? k1s : (qg == 2 ? v0s : v1s));
+  float* mine = reinterpret_cast<float*>(xbuf);
   if (kh == 1) {
 #pragma unroll
     for (int md = 0; md < 4; ++md)
@@ -318,19 +329,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, int L, int topk,
-                           const int32_t* block_idx, float scale, void* out, float* lse,
-                           hipStream_t stream) {
+                           const int32_t* block_idx, const int32_t* qblock_order, float scale, void* out,
+                           float* lse, hipStream_t stream) {
   const int n_blocks = L / kBlock;
   const int per_xcd = (n_blocks + kXcds - 1) / kXcds;
   const long long grid = (long long)kXcds * per_xcd * BH;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-  if (err != hipSuccess) return err;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), kLds, stream,
+  hipLaunchKernelGGL(fwd_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      static_cast<const unsigned char*>(q), static_cast<const unsigned char*>(k),
-                     static_cast<const unsigned char*>(v), block_idx, BH, L, n_blocks, topk, per_xcd,
+                     static_cast<const unsigned char*>(v), block_idx, qblock_order, BH, L, n_blocks, topk, per_xcd,
                      scale_log2, static_cast<unsigned char*>(out), lse);
   return hipGetLastError();
 }

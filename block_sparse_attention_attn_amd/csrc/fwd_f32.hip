@@ -18,13 +18,14 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ q,
                                                       const float* __restrict__ k,
                                                       const float* __restrict__ v,
-                                                      const int32_t* __restrict__ block_idx, int L,
+                                                      const int32_t* __restrict__ block_idx,
+                                                      const int32_t* __restrict__ qblock_order, int L,
                                                       int block, int n_blocks, int topk,
                                                       float scale, float* __restrict__ out,
                                                       float* __restrict__ lse) {
   __shared__ float ks[kChunk][D];
   __shared__ float vs[kChunk][D];
-  const int i = blockIdx.x;
+  const int i = qblock_order ? min(max(qblock_order[blockIdx.x], 0), n_blocks - 1) : (int)blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
   const bool active = tid < block;
@@ -79,16 +80,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH, int L, int d,
-                          int block, int topk, const int32_t* block_idx, float scale, float* out,
-                          float* lse, hipStream_t stream) {
+                          int block, int topk, const int32_t* block_idx, const int32_t* qblock_order,
+                          float scale, float* out, float* lse, hipStream_t stream) {
   const int n_blocks = L / block;
   dim3 grid(n_blocks, BH);
   const int threads = ((block + 63) / 64) * 64;
   if (d == 64)
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(threads), 0, stream, q, k, v, block_idx, L,
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(threads), 0, stream, q, k, v, block_idx, qblock_order, L,
                        block, n_blocks, topk, scale, out, lse);
   else
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(threads), 0, stream, q, k, v, block_idx, L,
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(threads), 0, stream, q, k, v, block_idx, qblock_order, L,
                        block, n_blocks, topk, scale, out, lse);
   return hipGetLastError();
 }

@@ -15,12 +15,12 @@ hipError_t launch_select(const double* q_pooled, const double* k_pooled, int BH,
 
 // Sparse attention, bf16 matrix-core path (d == block == 128).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, int L, int topk,
-                           const int32_t* block_idx, float scale, void* out, float* lse,
-                           hipStream_t stream);
+                           const int32_t* block_idx, const int32_t* qblock_order, float scale, void* out,
+                           float* lse, hipStream_t stream);
 
 // Sparse attention, fp32 path (d in {64,128}, block <= 256).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH, int L, int d,
-                          int block, int topk, const int32_t* block_idx, float scale, float* out,
-                          float* lse, hipStream_t stream);
+                          int block, int topk, const int32_t* block_idx, const int32_t* qblock_order,
+                          float scale, float* out, float* lse, hipStream_t stream);
 
 }  // namespace sol_attn

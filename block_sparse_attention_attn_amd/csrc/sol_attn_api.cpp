@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/sol_attn.h"
 #include "launchers.h"
@@ -92,8 +95,8 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
 }
 
 int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
-                 int block, int topk, const int32_t* block_idx, float softmax_scale, void* out,
-                 float* lse_or_null, void* stream) {
+                 int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                 float softmax_scale, void* out, float* lse_or_null, void* stream) {
   int st = check_common(dtype, B, H, L, d, block);
   if (st != SOL_ATTN_OK) return st;
   const bool bf16 = dtype == SOL_ATTN_BF16;
@@ -110,18 +113,40 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
   if (!q || !k || !v || !block_idx || !out) return fail(SOL_ATTN_ERR_NULL, "fwd: NULL pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(SOL_ATTN_ERR_ALIGN, "fwd: q/k/v/out not 16-byte aligned");
-  if (!aligned(block_idx, 4) || (lse_or_null && !aligned(lse_or_null, 4)))
-    return fail(SOL_ATTN_ERR_ALIGN, "fwd: block_idx/lse not 4-byte aligned");
+  if (!aligned(block_idx, 4) || (lse_or_null && !aligned(lse_or_null, 4)) ||
+      (qblock_order_or_null && !aligned(qblock_order_or_null, 4)))
+    return fail(SOL_ATTN_ERR_ALIGN, "fwd: block_idx/qblock_order/lse not 4-byte aligned");
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (bf16)
-    return hip_status(sol_attn::launch_fwd_bf16(q, k, v, (int)BH, L, topk, block_idx, scale, out,
-                                                lse_or_null, s),
+    return hip_status(sol_attn::launch_fwd_bf16(q, k, v, (int)BH, L, topk, block_idx, qblock_order_or_null,
+                                                scale, out, lse_or_null, s),
                       "fwd bf16 launch");
   return hip_status(sol_attn::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                              static_cast<const float*>(v), (int)BH, L, d, block, topk,
-                                             block_idx, scale, static_cast<float*>(out), lse_or_null, s),
+                                             block_idx, qblock_order_or_null, scale, static_cast<float*>(out),
+                                             lse_or_null, s),
                     "fwd fp32 launch");
+}
+
+int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
+  if (block <= 0 || L < 0 || L % block != 0 || frame_tokens <= 0 || row_tokens <= 0 ||
+      row_tokens > frame_tokens)
+    return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,
+                frame_tokens, row_tokens);
+  const int nb = L / block;
+  if (nb > 0 && !order_host) return fail(SOL_ATTN_ERR_NULL, "frame_order: NULL output");
+  std::vector<int32_t> idx(nb);
+  for (int i = 0; i < nb; ++i) idx[i] = i;
+  auto key = [&](int i) {
+    const long long tok = (long long)i * block;
+    const long long frame = tok / frame_tokens;
+    const long long row = (tok % frame_tokens) / row_tokens;
+    return std::make_pair(row, frame);
+  };
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return key(a) < key(b); });
+  for (int i = 0; i < nb; ++i) order_host[i] = idx[i];
+  return ok();
 }
 
 const char* sol_attn_last_error(void) { return g_last_error.c_str(); }

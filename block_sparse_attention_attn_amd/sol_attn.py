@@ -9,6 +9,7 @@ Calls (same names as the C ABI):
   sol_attn_pool(q, k, block)                         -> (q_pooled, k_pooled) float64 [B,H,L/block,d]
   sol_attn_select(q_pooled, k_pooled, topk, ...)     -> block_idx int32 [B,H,nB,topk] (+ scores)
   sol_attn_fwd(q, k, v, block_idx, block, ...)       -> out [B,H,L,d] (+ lse float32 [B,H,L])
+  sol_attn_frame_order(L, block, frame_tokens, row_tokens) -> int32 schedule of the query blocks
   sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
 """
 from __future__ import annotations
@@ -49,8 +50,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_pool.restype = i
     lib.sol_attn_select.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.sol_attn_select.restype = i
-    lib.sol_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, ctypes.c_float, vp, vp, vp]
+    lib.sol_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.sol_attn_fwd.restype = i
+    lib.sol_attn_frame_order.argtypes = [i, i, i, i, vp]
+    lib.sol_attn_frame_order.restype = i
     lib.sol_attn_last_error.argtypes = []
     lib.sol_attn_last_error.restype = ctypes.c_char_p
     lib.sol_attn_version.argtypes = []
@@ -126,9 +129,19 @@ def sol_attn_select(q_pooled: torch.Tensor, k_pooled: torch.Tensor, topk: int, r
     return (idx, scores) if return_scores else idx
 
 
+def sol_attn_frame_order(L: int, block: int, frame_tokens: int, row_tokens: int) -> torch.Tensor:
+    """Host-computed query-block schedule for frame-major video tokens (int32 CPU tensor)."""
+    lib = load_library()
+    nb = L // block if block > 0 else 0
+    order = torch.empty(max(nb, 0), dtype=torch.int32)
+    _check("sol_attn_frame_order", lib.sol_attn_frame_order(L, block, frame_tokens, row_tokens,
+                                                            order.data_ptr() if nb else None))
+    return order
+
+
 def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor, block: int,
                  softmax_scale: Optional[float] = None, return_lse: bool = False,
-                 out: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, qblock_order: Optional[torch.Tensor] = None):
     lib = load_library()
     _check_qkv(q, k, v)
     B, H, L, d = q.shape
@@ -140,19 +153,25 @@ def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: t
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
+    if qblock_order is not None:
+        if (qblock_order.dtype != torch.int32 or qblock_order.device != q.device or
+                qblock_order.numel() != (L // block if block > 0 else 0) or not qblock_order.is_contiguous()):
+            raise ValueError("qblock_order must be a contiguous int32 device tensor of L/block entries")
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
     _check("sol_attn_fwd", lib.sol_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, L, d, block, topk,
-                                            _ptr(block_idx), scale, _ptr(out), _ptr(lse), _stream(q)))
+                                            _ptr(block_idx), _ptr(qblock_order), scale, _ptr(out), _ptr(lse),
+                                            _stream(q)))
     return (out, lse) if return_lse else out
 
 
 def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, topk: int,
-                     softmax_scale: Optional[float] = None, return_lse: bool = False):
-    """Pool -> select -> fwd.  Returns out (and lse), plus nothing else; use the
-    individual calls to inspect the pooled tensors or the selected blocks."""
+                     softmax_scale: Optional[float] = None, return_lse: bool = False,
+                     qblock_order: Optional[torch.Tensor] = None):
+    """Pool -> select -> fwd.  Returns out (and lse); use the individual calls to
+    inspect the pooled tensors or the selected blocks."""
     qp, kp = sol_attn_pool(q, k, block)
     idx = sol_attn_select(qp, kp, topk)
-    return sol_attn_fwd(q, k, v, idx, block, softmax_scale, return_lse)
+    return sol_attn_fwd(q, k, v, idx, block, softmax_scale, return_lse, qblock_order=qblock_order)
 
 
 def version() -> int:

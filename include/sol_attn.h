@@ -97,6 +97,13 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
  *                  entries of a row must be distinct (sol_attn_select guarantees both).
  *                  Out-of-range entries are clamped into range instead of faulting; the
  *                  affected rows' results are then unspecified.
+ *   qblock_order_or_null
+ *                  optional int32 [L/block] device array: a permutation of the query blocks
+ *                  giving the order in which they are scheduled (shared by all (b,h)).
+ *                  It changes only which blocks run concurrently -- and so how often K/V
+ *                  tiles are re-read from cache rather than memory -- never the results.
+ *                  NULL = ascending.  Entries outside [0, L/block) are clamped; a non-
+ *                  permutation leaves some output rows unwritten.  See sol_attn_frame_order.
  *   softmax_scale  multiplier of q.k inside the softmax; <= 0 selects 1/sqrt(d).
  *   out            [B,H,L,d] of `dtype`: O = softmax(q K_sel^T * scale) V_sel per query row;
  *                  bf16 results are rounded to nearest-even from float32.
@@ -106,8 +113,21 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
  * and 1 <= block <= 256.  16-byte alignment for q,k,v,out; 4-byte for lse and block_idx.
  */
 int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
-                 int block, int topk, const int32_t* block_idx, float softmax_scale, void* out,
-                 float* lse_or_null, void* stream);
+                 int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                 float softmax_scale, void* out, float* lse_or_null, void* stream);
+
+/*
+ * Host helper (no GPU work): a query-block schedule for frame-major video tokens.
+ * Tokens are frame-major with `frame_tokens` tokens per latent frame and `row_tokens`
+ * per latent row (the latent grid of a clip is frames x rows x cols; Sol-H3-VAE model
+ * card, section "Usage").  Query blocks covering the same latent rows in different
+ * frames select similar key blocks, so the order sorts blocks by (row of their first
+ * token, frame, index): neighbouring entries then share K/V tiles in cache.
+ *   order_host  HOST int32 [L/block] output (caller-owned).
+ * Returns SOL_ATTN_ERR_SHAPE unless block > 0, L % block == 0, frame_tokens > 0 and
+ * 0 < row_tokens <= frame_tokens.
+ */
+int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host);
 
 /* Human-readable description of the last failure on the calling thread ("" if none). */
 const char* sol_attn_last_error(void);

@@ -20,7 +20,7 @@ def lib():
 def test_header_symbols_exported(lib):
     names = S.header_symbols()
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
-                          "sol_attn_version"}
+                          "sol_attn_version", "sol_attn_frame_order"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -35,8 +35,8 @@ MIS = FAKE + 2      # misaligned
 
 
 def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, H=1, L=256, d=128, block=128, topk=1, idx=FAKE,
-         out=FAKE, lse=None):
-    return lib.sol_attn_fwd(q, k, v, dtype, B, H, L, d, block, topk, idx, 0.0, out, lse, None)
+         out=FAKE, lse=None, order=None):
+    return lib.sol_attn_fwd(q, k, v, dtype, B, H, L, d, block, topk, idx, order, 0.0, out, lse, None)
 
 
 def test_fwd_argument_errors(lib):
@@ -55,6 +55,7 @@ def test_fwd_argument_errors(lib):
     assert _fwd(lib, out=None) == 1
     assert _fwd(lib, v=MIS) == 5
     assert _fwd(lib, lse=FAKE + 2) == 5
+    assert _fwd(lib, order=FAKE + 1) == 5
     assert b"topk" in lib.sol_attn_last_error() or b"aligned" in lib.sol_attn_last_error()
 
 
@@ -102,3 +103,21 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         S.sol_attn_pool(q, q, 128)
+
+
+def test_frame_order(lib):
+    import numpy as np
+    # 2 frames x 4 rows x 32 cols = 256 tokens, blocks of 32 tokens = one row each
+    o = S.sol_attn_frame_order(256, 32, 128, 32).numpy()
+    assert o.tolist() == [0, 4, 1, 5, 2, 6, 3, 7]          # row-major across frames
+    # blocks straddling rows: key = row of the first token
+    o = S.sol_attn_frame_order(4 * 84 * 48, 128, 48 * 84, 84).numpy()
+    assert sorted(o.tolist()) == list(range(4 * 84 * 48 // 128))   # a permutation
+    first = np.array(o) * 128
+    rows = (first % (48 * 84)) // 84
+    frames = first // (48 * 84)
+    keys = list(zip(rows, frames))
+    assert keys == sorted(keys)
+    assert lib.sol_attn_frame_order(100, 32, 64, 32, None) == 2        # L % block
+    assert lib.sol_attn_frame_order(128, 32, 64, 65, None) == 2        # row > frame
+    assert lib.sol_attn_frame_order(0, 32, 64, 32, None) == 0          # empty

@@ -187,6 +187,22 @@ def test_selection_invariant_under_within_block_permutation(S):
     assert np.array_equal(S.sol_attn_select(*S.sol_attn_pool(Q, Kp, 128), 4).cpu().numpy(), base)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_schedule_order_does_not_change_results(S, dtype):
+    """Any permutation of the query-block schedule gives bit-identical outputs."""
+    base = W.get("draft_896x512") if dtype == "bf16" else W.get("tiny_fp32_1k")
+    wl = dataclasses.replace(base, name="ord", H=2, frames=4, lat_h=8, lat_w=48 if dtype == "bf16" else 16,
+                             coarse=(2, 2, 3), topk=3, seed=13)
+    Q, K, V = (dev(x, dtype) for x in W.make_qkv(wl))
+    idx = S.sol_attn_select(*S.sol_attn_pool(Q, K, wl.block), 3)
+    nb = wl.L // wl.block
+    a = S.sol_attn_fwd(Q, K, V, idx, wl.block)
+    for order in (S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w),
+                  torch.randperm(nb, generator=torch.Generator().manual_seed(1)).to(torch.int32)):
+        b = S.sol_attn_fwd(Q, K, V, idx, wl.block, qblock_order=order.cuda())
+        assert torch.equal(a.view(torch.int16) if dtype == "bf16" else a, b.view(torch.int16) if dtype == "bf16" else b)
+
+
 def test_fwd_deterministic(S):
     wl = dataclasses.replace(W.get("draft_896x512"), name="det", H=3, frames=2, lat_h=16, lat_w=64, coarse=(1, 2, 4),
                              topk=3, seed=11)
@@ -209,10 +225,11 @@ def test_full_size_workload(S, name):
     q, k, v = W.make_qkv(wl)
     Q, K, V = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
     log(f"full {name}: gpu pool/select/fwd")
+    order = S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w).cuda()
     qp, kp = S.sol_attn_pool(Q, K, wl.block)
     idx = S.sol_attn_select(qp, kp, wl.topk)
     out = torch.full_like(Q, float("nan"))
-    S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out)
+    S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out, qblock_order=order)
     torch.cuda.synchronize()
     log(f"full {name}: oracle pool/select")
     Qd = oracle.widen(q, "bf16")
@@ -247,7 +264,7 @@ def test_full_size_workload(S, name):
         kd = wl.n_blocks
         idx_d = S.sol_attn_select(qp, kp, kd)
         assert torch.equal(idx_d[0, 0, 0].cpu(), torch.arange(kd, dtype=torch.int32))
-        S.sol_attn_fwd(Q, K, V, idx_d, wl.block, out=out)
+        S.sol_attn_fwd(Q, K, V, idx_d, wl.block, out=out, qblock_order=order)
         torch.cuda.synchronize()
         bh, i = 5, 17
         s = slice(i * wl.block, (i + 1) * wl.block)
