@@ -331,6 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, int L, int topk,
                            const int32_t* block_idx, const int32_t* qblock_order, float scale, void* out,
                            float* lse, hipStream_t stream) {
+  (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
   const int n_blocks = L / kBlock;
   const int per_xcd = (n_blocks + kXcds - 1) / kXcds;
   const long long grid = (long long)kXcds * per_xcd * BH;

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH, int L, int d,
                           int block, int topk, const int32_t* block_idx, const int32_t* qblock_order,
                           float scale, float* out, float* lse, hipStream_t stream) {
+  (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
   const int n_blocks = L / block;
   dim3 grid(n_blocks, BH);
   const int threads = ((block + 63) / 64) * 64;

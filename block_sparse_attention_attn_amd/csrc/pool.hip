@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 
 hipError_t launch_pool(const void* q, const void* k, bool is_bf16, int BH, int L, int d, int block,
                        double* q_pooled, double* k_pooled, hipStream_t stream) {
+  (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
   const int n_blocks = L / block;
   const int chunks_per_row = d / (is_bf16 ? 8 : 4);
   const int groups = kThreads / chunks_per_row;

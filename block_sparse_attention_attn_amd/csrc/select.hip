@@ -6,17 +6,25 @@
 // Per (b,h) and query block i:  r_ij = sum_e Qbar_ie * Kbar_je  (float64),
 // keep the `topk` largest r_ij with ties to the lower j, write them ascending.
 //
-// Work split: a workgroup owns R consecutive query blocks of one (b,h).
+// Two implementations share the top-k phase.  For d <= 128 and up to 1280 blocks
+// the scores come from float64 matrix-core tiles (see select_mfma_kernel);
+// otherwise from the general kernel below.
+//
+// General kernel: a workgroup (4 waves) owns R consecutive query blocks of one (b,h).
 //   1. Qbar rows of the group -> LDS.
-//   2. Each thread takes key blocks j = tid, tid+256, ...: streams Kbar_j once
-//      and forms the R dot products (float64 FMA), storing an order-preserving
-//      64-bit key of r_ij in LDS (and optionally r_ij/sqrt(d)).
+//   2. Kbar is streamed through LDS in chunks of 64 key blocks with coalesced
+//      16-byte loads (rows padded by one double so that 64 lanes reading the
+//      same column of 64 different rows hit distinct banks).  Lane l of a wave
+//      owns key block j = chunk + l and forms the dot products of its rows
+//      (float64 FMA; wave w takes rows w, w+4, ...), storing an order-preserving
+//      64-bit key of r_ij in LDS (and optionally r_ij / sqrt(d)).
 //   3. One wave per row finds the k-th largest key T by a 64-step bitwise
-//      search: at each step a candidate threshold is accepted if at least topk
-//      keys are >= it; counts come from wave ballots + popcount (no shuffles).
+//      search: a candidate threshold is accepted if at least topk keys are >= it;
+//      counts come from wave ballots + popcount.  Lane l owns keys j = 64*t + l.
 //   4. Keys > T are taken, plus the first (topk - #(>T)) keys == T in ascending
-//      j; positions come from two wave-wide exclusive scans over lanes that own
-//      contiguous ranges of j, so the output is ascending without sorting.
+//      j.  With interleaved ownership, ascending j is (t, lane) order, so a key's
+//      output position is a running count plus the popcount of the ballot bits
+//      of lower lanes: the output comes out ascending without a sort or scan.
 #include "launchers.h"
 
 namespace sol_attn {
@@ -26,6 +34,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxRows = 8;
 
+// key blocks staged per pass: 64 (one per lane) for d <= 128, fewer for larger d
+__host__ __device__ constexpr int chunk_for(int d) { return d <= 128 ? 64 : (d <= 256 ? 32 : 16); }
+
 // Order-preserving map float64 -> uint64 (larger r <=> larger key).  -0.0 is
 // first turned into +0.0 (x + 0.0) so that the two zeros rank as equal.
 __device__ __forceinline__ uint64_t order_key(double r) {
@@ -33,19 +44,94 @@ __device__ __forceinline__ uint64_t order_key(double r) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-__device__ __forceinline__ int wave_popcount(bool pred) {
-  return __popcll(__ballot(pred));
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_excl_scan(int x, int lane) {
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
+// Top-k of rows of order keys held in LDS ([nrows][n_blocks]); one wave per row,
+// lane owns key blocks j = 64*t + lane.  Writes `topk` ascending indices per row.
+__device__ __forceinline__ void topk_rows(const uint64_t* keys, int n_blocks, int topk, int nrows, int wave,
+                                          int lane, int32_t* __restrict__ out_rows) {
+  const int per_lane = (n_blocks + 63) / 64;
+  for (int r = wave; r < nrows; r += kWaves) {
+    const uint64_t* rk = keys + (size_t)r * n_blocks;
+    // k-th largest key value: the largest T with #(key >= T) >= topk (keys are >= 1)
+    uint64_t T = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = T | (1ull << bit);
+      int cnt = 0;
+      for (int t = 0; t < per_lane; ++t) {
+        const int j = 64 * t + lane;
+        const bool ge = j < n_blocks && rk[min(j, n_blocks - 1)] >= cand;
+        cnt += __popcll(__ballot(ge));
+      }
+      if (cnt >= topk) T = cand;
+    }
+    int tot_gt = 0;
+    for (int t = 0; t < per_lane; ++t) {
+      const int j = 64 * t + lane;
+      tot_gt += __popcll(__ballot(j < n_blocks && rk[min(j, n_blocks - 1)] > T));
+    }
+    const int need_eq = topk - tot_gt;     // >= 1 by the choice of T
+    int32_t* out = out_rows + (size_t)r * topk;
+    int base = 0, eq_seen = 0;
+    const uint64_t below = lanes_below(lane);
+    for (int t = 0; t < per_lane; ++t) {
+      const int j = 64 * t + lane;
+      const uint64_t x = j < n_blocks ? rk[j] : 0;
+      const bool gt = j < n_blocks && x > T;
+      const bool eq = j < n_blocks && x == T;
+      const uint64_t eq_mask = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + __popcll(eq_mask & below) < need_eq);
+      const uint64_t take_mask = __ballot(take);
+      if (take) out[base + __popcll(take_mask & below)] = j;
+      base += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
   }
-  return incl - x;
+}
+
+// Same as topk_rows, with each lane's keys (at most MAXPL) cached in registers,
+// so the 64 bisection steps touch no memory.
+template <int MAXPL>
+__device__ __forceinline__ void topk_rows_reg(const uint64_t* keys, int n_blocks, int topk, int nrows,
+                                              int wave, int lane, int32_t* __restrict__ out_rows) {
+  for (int r = wave; r < nrows; r += kWaves) {
+    const uint64_t* rk = keys + (size_t)r * n_blocks;
+    uint64_t x[MAXPL];
+#pragma unroll
+    for (int t = 0; t < MAXPL; ++t) {
+      const int j = 64 * t + lane;
+      x[t] = j < n_blocks ? rk[j] : 0;     // 0 ranks below every real key
+    }
+    uint64_t T = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = T | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < MAXPL; ++t) cnt += __popcll(__ballot(x[t] >= cand));
+      if (cnt >= topk) T = cand;
+    }
+    int tot_gt = 0;
+#pragma unroll
+    for (int t = 0; t < MAXPL; ++t) tot_gt += __popcll(__ballot(x[t] > T));
+    const int need_eq = topk - tot_gt;
+    int32_t* out = out_rows + (size_t)r * topk;
+    int base = 0, eq_seen = 0;
+    const uint64_t below = lanes_below(lane);
+#pragma unroll
+    for (int t = 0; t < MAXPL; ++t) {
+      const int j = 64 * t + lane;
+      const bool gt = x[t] > T;
+      const bool eq = x[t] == T && j < n_blocks;
+      const uint64_t eq_mask = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + __popcll(eq_mask & below) < need_eq);
+      const uint64_t take_mask = __ballot(take);
+      if (take) out[base + __popcll(take_mask & below)] = j;
+      base += __popcll(take_mask);
+      eq_seen += __popcll(eq_mask);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restrict__ q_pooled,
@@ -55,102 +141,158 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
                                                           double* __restrict__ scores,
                                                           double sqrt_d) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  double* qs = reinterpret_cast<double*>(smem);                          // [rows][d]
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem + (size_t)rows * d * 8);  // [rows][n_blocks]
+  const int dp = d + 1;                                                    // padded row length
+  const int kchunk = chunk_for(d);
+  double* qs = reinterpret_cast<double*>(smem);                            // [rows][d]
+  double* ks = qs + (size_t)rows * d;                                      // [kchunk][d+1]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ks + (size_t)kchunk * dp);  // [rows][n_blocks]
 
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * rows;
   const int nrows = min(rows, n_blocks - i0);
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double* qbase = q_pooled + ((size_t)bh * n_blocks + i0) * d;
   const double* kbase = k_pooled + (size_t)bh * n_blocks * d;
 
   for (int t = tid; t < nrows * d; t += kThreads) qs[t] = qbase[t];
-  __syncthreads();
 
-  // --- scores
-  for (int j = tid; j < n_blocks; j += kThreads) {
-    double acc[kMaxRows];
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0;
-    const double* kr = kbase + (size_t)j * d;
-    for (int e = 0; e < d; ++e) {
-      const double kv = kr[e];
-#pragma unroll
-      for (int r = 0; r < kMaxRows; ++r)
-        if (r < nrows) acc[r] = fma(qs[r * d + e], kv, acc[r]);
+  // --- scores, chunk by chunk of 64 key blocks
+  for (int j0 = 0; j0 < n_blocks; j0 += kchunk) {
+    const int nk = min(kchunk, n_blocks - j0);
+    __syncthreads();   // previous chunk fully consumed (and Qbar visible on the first pass)
+    // coalesced copy of Kbar[j0 .. j0+nk) (d doubles each) into the padded LDS rows
+    const double* src = kbase + (size_t)j0 * d;
+    for (int x = tid; x < nk * d; x += kThreads) {
+      const int jj = x / d, e = x - jj * d;
+      ks[jj * dp + e] = src[x];
     }
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) {
-      if (r < nrows) {
-        keys[(size_t)r * n_blocks + j] = order_key(acc[r]);
-        if (scores) scores[((size_t)bh * n_blocks + i0 + r) * n_blocks + j] = acc[r] / sqrt_d;
+    __syncthreads();
+    const int j = j0 + lane;
+    if (lane < nk) {
+      const double* kr = ks + lane * dp;
+      for (int r = wave; r < nrows; r += kWaves) {
+        const double* qr = qs + r * d;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e) acc = fma(qr[e], kr[e], acc);
+        keys[(size_t)r * n_blocks + j] = order_key(acc);
+        if (scores) scores[((size_t)bh * n_blocks + i0 + r) * n_blocks + j] = acc / sqrt_d;
       }
     }
   }
   __syncthreads();
 
-  // --- top-k per row, one wave per row
+  topk_rows(keys, n_blocks, topk, nrows, wave, lane, block_idx + ((size_t)bh * n_blocks + i0) * topk);
+}
+
+size_t select_lds_bytes(int rows, int n_blocks, int d) {
+  return ((size_t)rows * d + (size_t)chunk_for(d) * (d + 1) + (size_t)rows * n_blocks) * 8;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core path (d <= 128, n_blocks <= 1280): scores of 16 query rows x 16 key
+// blocks per v_mfma_f64_16x16x4_f64 chain.  For the 16x16x4 shape lane l supplies
+// A[l%16][l/16] and B[l/16][l%16] and receives D[4*r + l/16][l%16] in its
+// output register r = 0..3 (layout measured on gfx950).
+// The contraction index is permuted, e = (l/16)*S + s for step s (S = ceil(d/4)),
+// so every lane reads S contiguous doubles of its own Qbar row (kept in registers)
+// and of its key block's Kbar row (coalesced 16-byte loads).  Each score is one
+// fixed-order float64 FMA chain, so identical key blocks score identically.
+constexpr int kMfmaRows = 16;
+constexpr int kMaxMfmaBlocks = 1280;   // 16 rows of keys fill 160 KiB of LDS
+constexpr int kMaxS = 32;          // d <= 128
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <int MAXPL>
+__global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __restrict__ q_pooled,
+                                                               const double* __restrict__ k_pooled,
+                                                               int n_blocks, int d, int topk,
+                                                               int32_t* __restrict__ block_idx,
+                                                               double* __restrict__ scores,
+                                                               double sqrt_d) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);       // [16][n_blocks]
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * kMfmaRows;
+  const int nrows = min(kMfmaRows, n_blocks - i0);
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int per_lane = (n_blocks + 63) / 64;      // lane owns j in [lane*per_lane, +per_lane)
-  const int j_lo = lane * per_lane;
-  const int j_hi = min(n_blocks, j_lo + per_lane);
-  for (int r = wave; r < nrows; r += kWaves) {
-    const uint64_t* rk = keys + (size_t)r * n_blocks;
-    // k-th largest key value: the largest T with #(key >= T) >= topk
-    uint64_t T = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t cand = T | (1ull << bit);
-      int cnt = 0;
-      for (int t = 0; t < per_lane; ++t) {
-        const int j = j_lo + t;
-        const uint64_t x = rk[min(j, n_blocks - 1)];
-        cnt += wave_popcount(j < j_hi && x >= cand);
-      }
-      if (cnt >= topk) T = cand;
-    }
-    int n_gt = 0, n_eq = 0;
-    for (int j = j_lo; j < j_hi; ++j) {
-      const uint64_t x = rk[j];
-      n_gt += x > T;
-      n_eq += x == T;
-    }
-    // total keys > T across the wave
-    int tot_gt = n_gt;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = (d + 3) / 4;
+  const int col = lane & 15, kk = lane >> 4;
+  const int e0 = kk * S;
+
+  // A operand: Qbar[i0 + col][e0 + s]
+  double a[kMaxS];
+  {
+    const int row = min(i0 + col, n_blocks - 1);
+    const double* qr = q_pooled + ((size_t)bh * n_blocks + row) * d + e0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot_gt += __shfl_xor(tot_gt, off, 64);
-    const int need_eq = topk - tot_gt;               // >= 1 by the choice of T
-    int eq_before = wave_excl_scan(n_eq, lane);
-    // selected count per lane
-    int n_sel = n_gt + max(0, min(n_eq, need_eq - eq_before));
-    int pos = wave_excl_scan(n_sel, lane);
-    int32_t* out = block_idx + ((size_t)bh * n_blocks + i0 + r) * topk;
-    for (int j = j_lo; j < j_hi; ++j) {
-      const uint64_t x = rk[j];
-      bool take = x > T;
-      if (x == T) {
-        take = eq_before < need_eq;
-        ++eq_before;
+    for (int s = 0; s < kMaxS; ++s) a[s] = (s < S && e0 + s < d && col < nrows) ? qr[s] : 0.0;
+  }
+  const double* kbase = k_pooled + (size_t)bh * n_blocks * d;
+  for (int j0 = wave * 16; j0 < n_blocks; j0 += kWaves * 16) {
+    const int j = j0 + col;
+    const double* kr = kbase + (size_t)min(j, n_blocks - 1) * d + e0;
+    f64x4 c = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      if (s < S) {
+        const double b = (e0 + s < d && j < n_blocks) ? kr[s] : 0.0;
+        c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b, c, 0, 0, 0);
       }
-      if (take) out[pos++] = j;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * r + kk;
+      if (i < nrows && j < n_blocks) {
+        keys[(size_t)i * n_blocks + j] = order_key(c[r]);
+        if (scores) scores[((size_t)bh * n_blocks + i0 + i) * n_blocks + j] = c[r] / sqrt_d;
+      }
     }
   }
+  __syncthreads();
+  topk_rows_reg<MAXPL>(keys, n_blocks, topk, nrows, wave, lane, block_idx + ((size_t)bh * n_blocks + i0) * topk);
 }
 
 }  // namespace
 
 hipError_t launch_select(const double* q_pooled, const double* k_pooled, int BH, int n_blocks, int d,
                          int topk, int32_t* block_idx, double* scores_or_null, hipStream_t stream) {
-  // rows per workgroup: as many as fit (<= 8) with the key rows in <= 128 KiB of LDS
-  const size_t budget = 128 * 1024;
+  (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
+  const size_t budget = 160 * 1024;
+  if (d <= 4 * kMaxS && n_blocks <= kMaxMfmaBlocks) {
+    const size_t lds = (size_t)kMfmaRows * n_blocks * 8;
+    const int per_lane = (n_blocks + 63) / 64;
+    // keys cached per lane in the top-k phase: the smallest instantiation that holds them
+    auto kern = per_lane <= 4 ? select_mfma_kernel<4>
+              : per_lane <= 8 ? select_mfma_kernel<8>
+              : per_lane <= 16 ? select_mfma_kernel<16>
+              : select_mfma_kernel<(kMaxMfmaBlocks + 63) / 64>;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) {
+      (void)hipGetLastError();
+      return err;
+    }
+    dim3 grid((n_blocks + kMfmaRows - 1) / kMfmaRows, BH);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, q_pooled, k_pooled, n_blocks, d, topk, block_idx,
+                       scores_or_null, sqrt((double)d));
+    return hipGetLastError();
+  }
+  // general path: rows per workgroup as many as fit (<= 8) in 160 KiB of LDS
   int rows = kMaxRows;
-  while (rows > 1 && (size_t)rows * (n_blocks + d) * 8 > budget) --rows;
-  const size_t lds = (size_t)rows * (n_blocks + d) * 8;
+  while (rows > 1 && select_lds_bytes(rows, n_blocks, d) > budget) --rows;
+  const size_t lds = select_lds_bytes(rows, n_blocks, d);
+  if (lds > budget) return hipErrorInvalidValue;
   dim3 grid((n_blocks + rows - 1) / rows, BH);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return err;
+  }
   hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), lds, stream, q_pooled, k_pooled, n_blocks,
                      d, topk, rows, block_idx, scores_or_null, sqrt((double)d));
   return hipGetLastError();

@@ -79,7 +79,7 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
   if (B < 0 || H < 0 || n_blocks < 0) return fail(SOL_ATTN_ERR_SHAPE, "negative size");
   if (d <= 0) return fail(SOL_ATTN_ERR_SHAPE, "d=%d must be positive", d);
   if (d > 512) return fail(SOL_ATTN_ERR_UNSUPPORTED, "select needs d <= 512 (d=%d)", d);
-  if (n_blocks > 16384) return fail(SOL_ATTN_ERR_UNSUPPORTED, "select needs n_blocks <= 16384");
+  if (n_blocks > 8192) return fail(SOL_ATTN_ERR_UNSUPPORTED, "select needs n_blocks <= 8192");
   const long long BH = (long long)B * H;
   if (BH * n_blocks == 0) return ok();
   if (topk < 1 || topk > n_blocks)

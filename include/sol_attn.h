@@ -84,7 +84,7 @@ int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, 
  *                       Row (b,h,i) holds the first `topk` key blocks j in the order
  *                       (r_ij descending, j ascending), r_ij = sum_e Qbar_ie*Kbar_je in float64.
  *   scores_or_null      optional float64 [B,H,n_blocks,n_blocks] output of r_ij/sqrt(d).
- * Supported: 1 <= d <= 512, n_blocks <= 16384, 1 <= topk <= n_blocks.  -0.0 and +0.0 rank as equal.
+ * Supported: 1 <= d <= 512, n_blocks <= 8192, 1 <= topk <= n_blocks.  -0.0 and +0.0 rank as equal.
  * Rows whose scores contain NaN get an unspecified (but in-range) selection.
  */
 int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,

@@ -91,7 +91,7 @@ def test_select_argument_errors(lib):
     assert s(nb=-1) == 2
     assert s(d=0) == 2
     assert s(d=1000) == 4
-    assert s(nb=20000, topk=1) == 4
+    assert s(nb=8193, topk=1) == 4
     assert s(idx=None) == 1
     assert s(idx=FAKE + 2) == 5
     assert s(scores=FAKE + 4) == 5
