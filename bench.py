@@ -28,10 +28,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of one sol_attn_fwd launch on the headline workload, from rocprofv3
-# FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) scaled by the copy-kernel
-# calibration factor; None until measured for the current kernel.
-FWD_TRAFFIC_BYTES = None
+# Memory-side traffic of one sol_attn_fwd launch on the headline workload (bytes):
+# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are
+# what the same counters read for a plain copy of known size in the same command).
+# Set to None whenever the kernel changes until it is measured again.
+FWD_TRAFFIC_BYTES = (21_244_934 * 2 + 645_194) * 1024
 
 
 def parse():
@@ -42,6 +43,8 @@ def parse():
     p.add_argument("--workload", default="refine_1344x768")
     p.add_argument("--topk", type=int, default=None, help="override k (e.g. all blocks for a dense run)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="after timing, run one plain device copy of Q (size known) to calibrate traffic counters")
     p.add_argument("--cpu-sample-blocks", type=int, default=24,
                    help="query blocks of one head the CPU oracle attends for its baseline")
     return p.parse_args()
@@ -151,6 +154,10 @@ def main():
     t_pool = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     t_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     t_fwd = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    if args.copy_probe:
+        out.copy_(Q)
+        torch.cuda.synchronize()
 
     flops = wl.effective_flops(topk)
     value = flops / (ms_per_step * 1e-3) / 1e12
