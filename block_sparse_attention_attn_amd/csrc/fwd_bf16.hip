@@ -393,16 +393,12 @@ __device__ __forceinline__ void half_dma(unsigned char* lds, __amdgpu_buffer_rsr
   }
 }
 
-// Wait until this wave's copies of the step's half tiles have landed (with one
-// younger half tile allowed in flight when `one_ahead`) and its LDS reads are
-// done, then barrier.  The empty asm statements keep the compiler from moving
-// memory accesses across the barrier.
-__device__ __forceinline__ void wait_copies_and_barrier(bool one_ahead) {
-  if (one_ahead) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerHalf));
-  } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-  }
+// Wait until this wave's copies of the step's half tiles have landed (the one
+// younger half tile stays in flight) and its LDS reads are done, then barrier.  The
+// empty asm statements keep the compiler from moving memory accesses across the
+// barrier.
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerHalf));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -493,21 +489,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
   Cursor c_comp = c_copy;
 
   // ---- copy side: half tile w = 2 * (union position) + (key half)
-  int issued = 0, j_copy = 0;
+  int j_copy = 0;
   bool copy_done = false;
-  auto issue = [&](int w, unsigned char* buf) {
-    if (copy_done) return;
-    if ((w & 1) == 0) {
+  // Every step issues exactly two half-tile copies: past the end of the union the
+  // last tile is copied again into the free slot (never read).  A fixed count keeps
+  // the compiler's model of the copies in flight exact, so it adds no wait of its own
+  // before the LDS reads.
+  auto issue = [&](int w, unsigned char* buf) __attribute__((always_inline)) {
+    if (!copy_done && (w & 1) == 0) {
       int j;
       bool fa, fb;
-      if (!advance(c_copy, j, fa, fb)) {
-        copy_done = true;
-        return;
-      }
-      j_copy = j;
+      if (advance(c_copy, j, fa, fb)) j_copy = j; else copy_done = true;
     }
     half_dma(buf, k_rsrc, v_rsrc, j_copy * kTileBytes + (w & 1) * kHalfBytes, wave, lane);
-    issued = w + 1;
   };
 
   // ---- transpose-read offsets for V^T operands (see the single-block kernel)
@@ -599,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
         for (int r = 0; r < 16; ++r) o[md][r] *= st.alpha;
     }
   };
-  auto consume = [&](const unsigned char* h0, const unsigned char* h1) {
+  auto consume = [&](const unsigned char* h0, const unsigned char* h1) __attribute__((always_inline)) {
     f32x16 s0[2], s1[2];
     uint32_t pb0[4][4], pb1[4][4];
     Soft st0, st1;
@@ -656,10 +650,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
   // step u consumes half tiles 2u, 2u+1 (slots (2u)%5, (2u+1)%5) and refills the
   // two slots released by step u-1 with half tiles 2u+3, 2u+4
   bool use_a = false, use_b = false;
-  auto step = [&](int u, int s0, int s1, int r0, int r1) {
+  auto step = [&](int u, int s0, int s1, int r0, int r1) __attribute__((always_inline)) {
     int j;
     if (!advance(c_comp, j, use_a, use_b)) return false;
-    wait_copies_and_barrier(issued > 2 * u + 2);
+    wait_copies_and_barrier();
     issue(2 * u + 3, slot(r0));
     issue(2 * u + 4, slot(r1));
     if (myq >= 0 && (grp ? use_b : use_a)) consume(slot(s0), slot(s1));

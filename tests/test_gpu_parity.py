@@ -188,19 +188,34 @@ def test_selection_invariant_under_within_block_permutation(S):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_schedule_order_does_not_change_results(S, dtype):
-    """Any permutation of the query-block schedule gives bit-identical outputs."""
+def test_schedule_order(S, dtype):
+    """The query-block schedule changes only which blocks run together (and, for bf16,
+    which two blocks share their common key tiles): any permutation gives bit-identical
+    outputs, and every schedule matches the oracle."""
     base = W.get("draft_896x512") if dtype == "bf16" else W.get("tiny_fp32_1k")
     wl = dataclasses.replace(base, name="ord", H=2, frames=4, lat_h=8, lat_w=48 if dtype == "bf16" else 16,
                              coarse=(2, 2, 3), topk=3, seed=13)
-    Q, K, V = (dev(x, dtype) for x in W.make_qkv(wl))
+    q, k, v = W.make_qkv(wl)
+    Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     idx = S.sol_attn_select(*S.sol_attn_pool(Q, K, wl.block), 3)
     nb = wl.L // wl.block
+    ref = oracle.run(q, k, v, dtype, wl.block, 3)
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
     a = S.sol_attn_fwd(Q, K, V, idx, wl.block)
-    for order in (S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w),
+    for order in (None, S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w),
                   torch.randperm(nb, generator=torch.Generator().manual_seed(1)).to(torch.int32)):
-        b = S.sol_attn_fwd(Q, K, V, idx, wl.block, qblock_order=order.cuda())
-        assert torch.equal(a.view(torch.int16) if dtype == "bf16" else a, b.view(torch.int16) if dtype == "bf16" else b)
+        b, lse = S.sol_attn_fwd(Q, K, V, idx, wl.block, qblock_order=None if order is None else order.cuda(),
+                                return_lse=True)
+        torch.cuda.synchronize()
+        err = np.abs(host_f64(b) - ref["out"])
+        lerr = np.abs(lse.double().cpu().numpy() - ref["lse"])
+        if dtype == "fp32":
+            assert torch.equal(a, b)
+            assert err.max() <= FP32_MAX
+        else:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+            assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+            assert lerr.max() <= 1e-2, lerr.max()
 
 
 def test_fwd_deterministic(S):
