@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="refine_1344x768")
     p.add_argument("--topk", type=int, default=None, help="override k (e.g. all blocks for a dense run)")
+    p.add_argument("--pattern", choices=["selected", "window"], default="selected",
+                   help="selected: pool -> select -> fwd (the method); window: fwd alone with the static "
+                        "window pattern of sol_attn_window_blocks (same k)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="after timing, run one plain device copy of Q (size known) to calibrate traffic counters")
@@ -50,9 +53,10 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(wl, q, k, v, topk, n_heads):
+def cpu_baseline(wl, q, k, v, topk, n_heads, pattern="selected"):
     """Time the float64 oracle as it stands -- pool, select and attend, every query
-    block -- on the first `n_heads` (b, h) heads of the workload."""
+    block (or, for the static window pattern, attend alone) -- on the first `n_heads`
+    (b, h) heads of the workload."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -63,13 +67,19 @@ def cpu_baseline(wl, q, k, v, topk, n_heads):
     ks = k.reshape(-1, wl.L, wl.d)[:n_heads]
     vs = v.reshape(-1, wl.L, wl.d)[:n_heads]
     t0 = time.perf_counter()
-    oracle.run(qs, ks, vs, wl.dtype, wl.block, topk)
+    if pattern == "window":
+        sel = np.broadcast_to(oracle.window_selection(wl.n_blocks, topk), (n_heads, wl.n_blocks, topk))
+        oracle.attend(oracle.widen(qs, wl.dtype), oracle.widen(ks, wl.dtype), oracle.widen(vs, wl.dtype), sel,
+                      wl.block)
+        what = f"float64 attention of all {wl.n_blocks} query blocks over the static window of {topk} blocks"
+    else:
+        oracle.run(qs, ks, vs, wl.dtype, wl.block, topk)
+        what = (f"whole path (pool, scores, top-{topk}, float64 attention of all {wl.n_blocks} query blocks)")
     dt = time.perf_counter() - t0
     flops = 4.0 * n_heads * wl.L * (topk * wl.block) * wl.d
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": f"{n_heads} of {wl.B * wl.H} heads, whole path (pool, scores, top-{topk}, float64 "
-                      f"attention of all {wl.n_blocks} query blocks); TFLOP/s in the same effective-flop count"}
+            "sample": f"{n_heads} of {wl.B * wl.H} heads, {what}; TFLOP/s in the same effective-flop count"}
 
 
 def main():
@@ -108,7 +118,20 @@ def main():
     dtc = 0 if wl.dtype == "bf16" else 1
     s_ptr = stream.cuda_stream
 
+    window = args.pattern == "window"
+    if window:
+        idx.copy_(S.sol_attn_window_blocks(nb, topk).view(1, 1, nb, topk).expand(wl.B, wl.H, nb, topk))
+
     def step(ev=None):
+        if window:   # static pattern: the step is the attention alone
+            for e in (ev or [])[:3]:
+                e.record(stream)
+            S._check("fwd", lib.sol_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dtc, wl.B, wl.H, wl.L,
+                                             wl.d, wl.block, topk, idx.data_ptr(), order.data_ptr(), 0.0,
+                                             out.data_ptr(), None, s_ptr))
+            if ev is not None:
+                ev[3].record(stream)
+            return
         if ev is not None:
             ev[0].record(stream)
         S._check("pool", lib.sol_attn_pool(Q.data_ptr(), K.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d, wl.block,
@@ -170,20 +193,22 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded smooth field + noise, unit RMS)",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d, "block": wl.block,
-                   "topk": topk, "n_blocks": nb, "latent": [wl.frames, wl.lat_h, wl.lat_w]},
+        "config": {"workload": wl.name + ("+window" if window else ""), "B": wl.B, "H": wl.H, "L": wl.L,
+                   "d": wl.d, "block": wl.block, "topk": topk, "n_blocks": nb,
+                   "latent": [wl.frames, wl.lat_h, wl.lat_w], "pattern": args.pattern},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"pool": round(t_pool, 4), "select": round(t_sel, 4), "fwd": round(t_fwd, 4)},
         "fwd_tflops": round(fwd_tflops, 2),
-        "pool_gbs": round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
+        "pool_gbs": None if window else round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": FWD_TRAFFIC_BYTES if (wl.name == "refine_1344x768" and topk == wl.topk) else None},
+                     "traffic": FWD_TRAFFIC_BYTES if (wl.name == "refine_1344x768" and topk == wl.topk
+                                                      and not window) else None},
         "timed_wall_s": round(wall, 3),
         "input_gen_s": round(t_gen, 2),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_heads)
+        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_heads, args.pattern)
     print(json.dumps(rec), flush=True)
 
 

@@ -149,6 +149,19 @@ int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int
   return ok();
 }
 
+int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host) {
+  if (n_blocks < 0) return fail(SOL_ATTN_ERR_SHAPE, "window_blocks: n_blocks=%d < 0", n_blocks);
+  if (n_blocks == 0) return ok();
+  if (topk < 1 || topk > n_blocks)
+    return fail(SOL_ATTN_ERR_K, "window_blocks: topk=%d outside [1, %d]", topk, n_blocks);
+  if (!idx_host) return fail(SOL_ATTN_ERR_NULL, "window_blocks: NULL output");
+  for (int i = 0; i < n_blocks; ++i) {
+    const int start = std::min(std::max(i - (topk - 1) / 2, 0), n_blocks - topk);
+    for (int t = 0; t < topk; ++t) idx_host[(size_t)i * topk + t] = start + t;
+  }
+  return ok();
+}
+
 const char* sol_attn_last_error(void) { return g_last_error.c_str(); }
 
 int sol_attn_version(void) { return SOL_ATTN_VERSION; }

@@ -10,6 +10,7 @@ Calls (same names as the C ABI):
   sol_attn_select(q_pooled, k_pooled, topk, ...)     -> block_idx int32 [B,H,nB,topk] (+ scores)
   sol_attn_fwd(q, k, v, block_idx, block, ...)       -> out [B,H,L,d] (+ lse float32 [B,H,L])
   sol_attn_frame_order(L, block, frame_tokens, row_tokens) -> int32 schedule of the query blocks
+  sol_attn_window_blocks(n_blocks, topk)             -> int32 [n_blocks, topk] static window pattern
   sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
 """
 from __future__ import annotations
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_fwd.restype = i
     lib.sol_attn_frame_order.argtypes = [i, i, i, i, vp]
     lib.sol_attn_frame_order.restype = i
+    lib.sol_attn_window_blocks.argtypes = [i, i, vp]
+    lib.sol_attn_window_blocks.restype = i
     lib.sol_attn_last_error.argtypes = []
     lib.sol_attn_last_error.restype = ctypes.c_char_p
     lib.sol_attn_version.argtypes = []
@@ -137,6 +140,15 @@ def sol_attn_frame_order(L: int, block: int, frame_tokens: int, row_tokens: int)
     _check("sol_attn_frame_order", lib.sol_attn_frame_order(L, block, frame_tokens, row_tokens,
                                                             order.data_ptr() if nb else None))
     return order
+
+
+def sol_attn_window_blocks(n_blocks: int, topk: int) -> torch.Tensor:
+    """Host-computed static window pattern: int32 CPU tensor [n_blocks, topk] (see the C header)."""
+    lib = load_library()
+    idx = torch.empty((max(n_blocks, 0), max(topk, 0)), dtype=torch.int32)
+    _check("sol_attn_window_blocks", lib.sol_attn_window_blocks(n_blocks, topk,
+                                                                idx.data_ptr() if idx.numel() else None))
+    return idx
 
 
 def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor, block: int,

@@ -129,6 +129,22 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
  */
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host);
 
+/*
+ * Host helper (no GPU work): a static block-sparse pattern for sol_attn_fwd, the
+ * decoder-style windowed attention (Sol-H3-VAE model card: whole frames with windowed
+ * attention, each native 5-latent block decoded bidirectionally) expressed as a fixed
+ * key-block list.  Query block i attends to the `topk` consecutive key blocks
+ * [s, s + topk) with s = clamp(i - (topk - 1) / 2, 0, n_blocks - topk): a window of
+ * frame-major tokens centred on the query block (for even topk one more block after it
+ * than before it) and shifted inwards at the ends, so every row has exactly topk
+ * entries, contains i and is ascending.
+ *   idx_host  HOST int32 [n_blocks][topk] output (caller-owned); pass it (copied to the
+ *             device, once per (b, h)) as block_idx of sol_attn_fwd.
+ * Returns SOL_ATTN_ERR_SHAPE if n_blocks < 0, SOL_ATTN_ERR_K unless 1 <= topk <= n_blocks
+ * (when n_blocks > 0), SOL_ATTN_ERR_NULL for a NULL output with n_blocks > 0.
+ */
+int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
+
 /* Human-readable description of the last failure on the calling thread ("" if none). */
 const char* sol_attn_last_error(void);
 

@@ -142,6 +142,22 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, block: 
     return O.reshape(*lead, L, d), lse.reshape(*lead, L)
 
 
+def window_selection(n_blocks: int, topk: int) -> np.ndarray:
+    """Static window pattern (the decoder's windowed attention as a fixed key-block list;
+    Sol-H3-VAE model card, opening paragraph).  Reading: row i holds the topk consecutive
+    key blocks whose centre is nearest to i -- for even topk two windows are equally
+    near and the later one is taken (one more block after i than before it) -- shifted
+    inwards at the two ends of the sequence.  Written as a search over all starts."""
+    starts = np.arange(n_blocks - topk + 1)
+    centres = starts + (topk - 1) / 2.0
+    out = np.empty((n_blocks, topk), dtype=np.int32)
+    for i in range(n_blocks):
+        dist = np.abs(centres - i)
+        s = starts[np.flatnonzero(dist == dist.min())[-1]]
+        out[i] = np.arange(s, s + topk)
+    return out
+
+
 def selection_margins(Qbar: np.ndarray, Kbar: np.ndarray, topk: int):
     """Certificate that the float64 selection equals the exact-arithmetic selection.
 

@@ -20,7 +20,7 @@ def lib():
 def test_header_symbols_exported(lib):
     names = S.header_symbols()
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
-                          "sol_attn_version", "sol_attn_frame_order"}
+                          "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
