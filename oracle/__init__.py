@@ -6,6 +6,6 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 it; the library's compute path never does, and the two share no code.
 """
 from .sol_attn_oracle import (  # noqa: F401
-    widen, pool, block_scores, select, select_from_scores, attend, attend_block,
+    widen, n_blocks, block_rows, pool, block_scores, select, select_from_scores, attend, attend_block,
     selection_margins, run, window_selection,
 )

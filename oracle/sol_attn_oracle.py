@@ -14,7 +14,9 @@ MiniMax H3 ...", first paragraph).
 The concrete reading implemented (the pages give no formula)
 -----------------------------------------------------------
 * tokens are frame-major; the sequence is cut into contiguous blocks of Bs tokens;
-* every query block and key block is mean-pooled (block sum / Bs);
+  when Bs does not divide L the last block holds the remaining L - (nB-1) Bs tokens
+  (nB = ceil(L / Bs));
+* every query block and key block is mean-pooled (block sum / number of its tokens);
 * pooled score of (query block i, key block j) is r_ij / sqrt(d), r_ij = Qbar_i . Kbar_j;
 * each query block keeps the k key blocks with the largest score, ties going to
   the lower key-block index; indices are emitted in ascending order;
@@ -36,8 +38,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-__all__ = ["widen", "pool", "block_scores", "select", "select_from_scores", "attend",
-           "attend_block", "selection_margins", "run"]
+__all__ = ["widen", "n_blocks", "block_rows", "pool", "block_scores", "select", "select_from_scores",
+           "attend", "attend_block", "selection_margins", "run", "window_selection"]
 
 
 def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
@@ -50,14 +52,25 @@ def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def n_blocks(L: int, block: int) -> int:
+    """Number of blocks: the last one may be shorter (ceil(L / block))."""
+    return -(-L // block)
+
+
+def block_rows(i: int, L: int, block: int) -> slice:
+    """Token rows of block i: [i*block, min((i+1)*block, L))."""
+    return slice(i * block, min((i + 1) * block, L))
+
+
 def pool(X: np.ndarray, block: int) -> np.ndarray:
-    """Block mean: [..., L, d] -> [..., L/block, d], Xbar_i = (sum of the block's rows) / block."""
+    """Block mean: [..., L, d] -> [..., nB, d], Xbar_i = (sum of block i's rows) / (its row count)."""
     *lead, L, d = X.shape
-    if L % block:
-        raise ValueError("L must be a multiple of the block size")
-    nb = L // block
-    sums = X.reshape(*lead, nb, block, d).sum(axis=-2)
-    return sums / block
+    nb = n_blocks(L, block)
+    out = np.empty((*lead, nb, d), dtype=np.float64)
+    for i in range(nb):
+        rows = X[..., block_rows(i, L, block), :]
+        out[..., i, :] = rows.sum(axis=-2) / rows.shape[-2]
+    return out
 
 
 def block_scores(Qbar: np.ndarray, Kbar: np.ndarray, chunk: int = 64) -> np.ndarray:
@@ -100,11 +113,12 @@ def attend_block(Qi: np.ndarray, K: np.ndarray, V: np.ndarray, sel_i: np.ndarray
                  scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Exact softmax attention of the rows of one query block over its selected key blocks.
 
-    Qi [Bs, d]; K, V [L, d] of the same (b, h); sel_i [k] key-block indices.
+    Qi [rows of the block, d]; K, V [L, d] of the same (b, h); sel_i [k] key-block indices.
     Returns (O_i [Bs, d], lse_i [Bs]) with lse = m + ln(sum exp(z - m)).
     """
     d = K.shape[-1]
     rows = (sel_i[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    rows = rows[rows < K.shape[0]]           # a short last block has only its own tokens
     Kc = K[rows]
     Vc = V[rows]
     z = (Qi @ Kc.T) * scale                  # [Bs, k*Bs]
@@ -127,7 +141,7 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, block: 
     *lead, L, d = Q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nb = L // block
+    nb = n_blocks(L, block)
     Qf = Q.reshape(-1, L, d)
     Kf = K.reshape(-1, L, d)
     Vf = V.reshape(-1, L, d)
@@ -137,7 +151,7 @@ def attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray, block: 
     blocks = range(nb) if qblocks is None else qblocks
     for bh in range(Qf.shape[0]):
         for i in blocks:
-            s = slice(i * block, (i + 1) * block)
+            s = block_rows(i, L, block)
             O[bh, s], lse[bh, s] = attend_block(Qf[bh, s], Kf[bh], Vf[bh], sf[bh, i], block, scale)
     return O.reshape(*lead, L, d), lse.reshape(*lead, L)
 

@@ -313,3 +313,50 @@ def test_margin_certificate_on_tiny_and_ties():
     Qb = np.array([[1.0, 2.0]])
     Kb = np.array([[1.0, 1.0], [3.0, 0.0], [0.0, 0.0]])
     assert oracle.selection_margins(Qb, Kb, 1)[2] == 1     # r = 3, 3, 0: exact tie at k=1
+
+
+# ----------------------------------------------------------------------------- ragged last block
+@pytest.mark.parametrize("L", [97, 100, 111, 113])
+def test_ragged_pool_is_mean_of_remaining_tokens(L):
+    """Block size 16 that does not divide L: the last block is the remaining L - 16(nB-1)
+    tokens and its mean is their exact sum (math.fsum) divided by their count."""
+    Bs, d = 16, 5
+    X = np.round(_rand((2, L, d), 7) * 64) / 64          # dyadic values: sums are exact
+    P = oracle.pool(X, Bs)
+    nb = -(-L // Bs)
+    assert P.shape == (2, nb, d) and oracle.n_blocks(L, Bs) == nb
+    last = L - (nb - 1) * Bs
+    for b in range(2):
+        for e in range(d):
+            assert P[b, nb - 1, e] == math.fsum(X[b, L - last:, e]) / last
+            for i in range(nb - 1):
+                assert P[b, i, e] == math.fsum(X[b, i * Bs:(i + 1) * Bs, e]) / Bs
+
+
+@pytest.mark.parametrize("L", [97, 120, 127])
+def test_ragged_k_all_equals_dense_attention(L):
+    """Short last block and k = nB: every query (all L rows) sees exactly the L keys, so the
+    oracle must equal dense softmax attention over the L tokens (torch, float64)."""
+    Bs, d = 16, 8
+    rng = np.random.default_rng(L)
+    Q, K, V = (rng.standard_normal((1, 2, L, d)) for _ in range(3))
+    nb = oracle.n_blocks(L, Bs)
+    idx = oracle.select(oracle.pool(Q, Bs), oracle.pool(K, Bs), nb)
+    assert np.array_equal(idx[0, 0, 0], np.arange(nb))
+    O, lse = oracle.attend(Q, K, V, idx, Bs)
+    assert not np.isnan(O).any()
+    assert np.max(np.abs(O - _dense_sdpa(Q, K, V))) <= 1e-12
+    z = np.einsum("bhld,bhmd->bhlm", Q, K) / math.sqrt(d)
+    assert np.max(np.abs(lse - torch.logsumexp(torch.from_numpy(z), dim=-1).numpy())) <= 1e-12
+
+
+def test_ragged_selected_short_block_contributes_only_its_tokens():
+    """A query block that selects the short last block attends to exactly its tokens plus
+    those of its other blocks: dense attention over that gathered key set."""
+    Bs, d, L = 16, 6, 70                                 # blocks 0..4, the last one has 6 tokens
+    rng = np.random.default_rng(3)
+    Q, K, V = (rng.standard_normal((1, 1, L, d)) for _ in range(3))
+    sel = np.array([[[1, 4]] * 5], dtype=np.int32)
+    O, _ = oracle.attend(Q, K, V, sel, Bs)
+    rows = np.r_[16:32, 64:70]
+    assert np.max(np.abs(O - _dense_sdpa(Q, K[..., rows, :], V[..., rows, :]))) <= 1e-12
