@@ -93,17 +93,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // 4s + l/16, so it fetches the logical chunk that the swizzle places there; the
 // 16 lanes of a row still read that row's 256 contiguous bytes.  Wave w copies
 // segments w, w+8, w+16, w+24.  Completion is awaited by the next barrier.
-__device__ __forceinline__ void tile_dma(unsigned char* lds, const unsigned char* __restrict__ g,
-                                         int wave, int lane) {
+// Buffer resource of one head's K or V (raw, byte-addressed, range-checked: rows past
+// the end of the head -- the missing rows of a short last block -- read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const unsigned char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off, int wave,
+                                         int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int seg = wave + 8 * i;
     const int row = 4 * seg + (lane >> 4);
     const int c = (lane & 15) ^ swz(row);
-    __builtin_amdgcn_global_load_lds(
-        static_cast<const void*>(g + (size_t)row * 256 + c * 16),
-        (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16,
+                                             off + row * 256 + c * 16, 0, 0, 0);
   }
+}
+
+// Scores of keys past the end of the sequence (a short last key block) -> -inf.
+// s[mb][r] holds key key0 + 32mb + 8(r/4) + 4h + r%4 of the tile; `valid` keys exist.
+__device__ __forceinline__ void mask_missing_keys(f32x16 (&s)[2], int key0, int h, int valid) {
+  int lim = valid - key0 - 4 * h;   // key offsets 32mb + 8(r/4) + r%4 from here on are missing
+  asm volatile("" : "+v"(lim));    // computed here, not hoisted as one value per register
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[mb][r] = 32 * mb + 8 * (r >> 2) + (r & 3) >= lim ? -INFINITY : s[mb][r];
 }
 
 // S^T (64 keys of this wave's half x 32 queries) = K_half . Q^T.
@@ -164,19 +180,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int key0 = 64 * kh;
 
   const size_t head_off = (size_t)bh * L * kD * 2;    // bytes
-  const unsigned char* kh_ptr = k + head_off;
-  const unsigned char* vh_ptr = v + head_off;
+  const __amdgpu_buffer_rsrc_t k_rsrc = head_rsrc(k + head_off, L * kD * 2);
+  const __amdgpu_buffer_rsrc_t v_rsrc = head_rsrc(v + head_off, L * kD * 2);
   const int32_t* sel = block_idx + ((size_t)bh * n_blocks + qb) * topk;
-  auto tile_src = [&](const unsigned char* base, int t) {
-    const int j = min(max(sel[t], 0), n_blocks - 1);
-    return base + (size_t)j * kTileBytes;
-  };
+  auto tile_block = [&](int t) { return min(max(sel[t], 0), n_blocks - 1); };
 
   // ---- Q^T operand: lane holds Q[query n][16*ks + 8*h + 0..7] for ks = 0..7
+  // (rows past the end of a short last block load the last row and are not stored)
   const int qrow = qb * kBlock + qg * 32 + n;
   bf16x8 qf[8];
   {
-    const unsigned char* qp = q + head_off + (size_t)qrow * kD * 2;
+    const unsigned char* qp = q + head_off + (size_t)min(qrow, L - 1) * kD * 2;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (16 * ks + 8 * h) * 2);
   }
@@ -206,9 +220,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   // ---- prologue: K0, V0, K1 into LDS; S_0
-  tile_dma(kbuf(0), tile_src(kh_ptr, 0), wave, lane);
-  tile_dma(vbuf(0), tile_src(vh_ptr, 0), wave, lane);
-  if (topk > 1) tile_dma(kbuf(1), tile_src(kh_ptr, 1), wave, lane);
+  tile_dma(kbuf(0), k_rsrc, tile_block(0) * kTileBytes, wave, lane);
+  tile_dma(vbuf(0), v_rsrc, tile_block(0) * kTileBytes, wave, lane);
+  if (topk > 1) tile_dma(kbuf(1), k_rsrc, tile_block(1) * kTileBytes, wave, lane);
   __syncthreads();
   f32x16 sa[2], sb[2];
   compute_st(sa, kbuf(0), key0, qf, n, h);
@@ -217,29 +231,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int t, int par) {
     const bool has_next = t + 1 < topk;
     // refill the buffers freed by the previous iteration: K_{t+2} and V_{t+1}
-    if (t + 2 < topk) tile_dma(kbuf(par), tile_src(kh_ptr, t + 2), wave, lane);
-    if (has_next) tile_dma(vbuf(par ^ 1), tile_src(vh_ptr, t + 1), wave, lane);
+    if (t + 2 < topk) tile_dma(kbuf(par), k_rsrc, tile_block(t + 2) * kTileBytes, wave, lane);
+    if (has_next) tile_dma(vbuf(par ^ 1), v_rsrc, tile_block(t + 1) * kTileBytes, wave, lane);
     // key half 0 computes the next S first, key half 1 after its softmax
     if (kh == 0 && has_next) compute_st(snext, kbuf(par ^ 1), key0, qf, n, h);
 
     // softmax on S_t (log2 domain)
+    const int valid = L - tile_block(t) * kBlock;   // keys of the tile that exist (short last block)
+    if (valid < kBlock) mask_missing_keys(scur, key0, h, valid);
     float mx = scur[0][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[mb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // a key half with no existing key yet keeps m = -inf, weights 0 and alpha 1
     const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
+    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
     float lsum = 0.f;
     uint32_t pb[4][4];   // P^T operand per k-step (8 bf16 = 4 dwords)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r], scale_log2, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r + 1], scale_log2, -m_new));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r], scale_log2, -m_sub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r + 1], scale_log2, -m_sub));
         lsum += p0 + p1;
         // register r of block mb holds key key0 + 32mb + 8(r/4) + 4h + r%4;
         // k-step ks = 2mb + r/8 takes r/4 even -> dwords 0,1 ; odd -> dwords 2,3
@@ -284,6 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     __syncthreads();   // also waits for this iteration's tile copies
   };
 
+  // the last step is peeled: only it can meet the short last block (the largest index)
   int t = 0;
   for (; t + 1 < topk; t += 2) {
     step(sa, sb, t, 0);
@@ -312,6 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const float l_tot = l_lane + __shfl_xor(l_lane, 32, 64);
   const float inv = 1.f / l_tot;
   const float c0 = a0 * inv, c1 = a1 * inv;
+  if (qrow >= L) return;   // past the end of a short last block
   unsigned char* op = out + head_off + (size_t)qrow * kD * 2;
 #pragma unroll
   for (int md = 0; md < 4; ++md)
@@ -370,10 +390,6 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
-// Buffer resource of one head's K or V (raw, byte-addressed, range-checked).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const unsigned char* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, bytes, 0x00020000);
-}
 
 // Copy 64 rows of K and the same 64 rows of V into one slot (wave w: segments w, w+8),
 // starting at byte `off` of the head.  MUBUF direct-to-LDS loads: unlike the FLAT
@@ -442,11 +458,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
   const __amdgpu_buffer_rsrc_t k_rsrc = head_rsrc(k + head_off, L * kD * 2);
   const __amdgpu_buffer_rsrc_t v_rsrc = head_rsrc(v + head_off, L * kD * 2);
 
-  // ---- Q^T operand of the wave's 32 queries (loaded before any tile copy)
+  // ---- Q^T operand of the wave's 32 queries (loaded before any tile copy; rows past
+  // the end of a short last block load the last row and are not stored)
   const int qrow = (myq >= 0 ? myq : 0) * kBlock + qg * 32 + n;
   bf16x8 qf[8];
   {
-    const unsigned char* qp = q + head_off + (size_t)qrow * kD * 2;
+    const unsigned char* qp = q + head_off + (size_t)min(qrow, L - 1) * kD * 2;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (16 * ks + 8 * h) * 2);
   }
@@ -474,6 +491,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
     return x;
   };
   auto head = [&](const int (&lst)[kListRegs], int i, int cnt) { return i < cnt ? entry(lst, i) : kNoBlock; };
+  // A short last block (L not a multiple of 128) is the last entry of any selection
+  // that contains it; it is left out of the main walk and handled after it with its
+  // missing keys masked, so the main loop carries no masking code.
+  const int last = n_blocks - 1;
+  const bool short_last = L % kBlock != 0;
+  const bool short_a = short_last && entry(la, topk - 1) == last;
+  const bool short_b = short_last && nsel_b > 0 && entry(lb, nsel_b - 1) == last;
+  const int cnt_a = topk - (short_a ? 1 : 0), cnt_b = nsel_b - (short_b ? 1 : 0);
   struct Cursor { int ia, ib, ja, jb; };
   // merge step: the smaller head (both when equal) is the next tile of the union
   auto advance = [&](Cursor& c, int& j, bool& fa, bool& fb) {
@@ -481,11 +506,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
     if (j == kNoBlock) return false;
     fa = c.ja == j;
     fb = c.jb == j;
-    if (fa) c.ja = head(la, ++c.ia, topk);
-    if (fb) c.jb = head(lb, ++c.ib, nsel_b);
+    if (fa) c.ja = head(la, ++c.ia, cnt_a);
+    if (fb) c.jb = head(lb, ++c.ib, cnt_b);
     return true;
   };
-  Cursor c_copy{0, 0, head(la, 0, topk), head(lb, 0, nsel_b)};
+  Cursor c_copy{0, 0, head(la, 0, cnt_a), head(lb, 0, cnt_b)};
   Cursor c_comp = c_copy;
 
   // ---- copy side: half tile w = 2 * (union position) + (key half)
@@ -561,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
       const float mx = fmaxf(st.mx, st.other) * scale_log2;
       st.up = mx > m_use + kRescaleSlack;
       const float m_new = st.up ? mx : m_use;
-      st.alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      st.alpha = st.up ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
       m_use = m_new;
       st.lsum = 0.f;
       pin(m_use);
@@ -593,7 +618,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
         for (int r = 0; r < 16; ++r) o[md][r] *= st.alpha;
     }
   };
-  auto consume = [&](const unsigned char* h0, const unsigned char* h1) __attribute__((always_inline)) {
+  // MASK (compile-time): the tile is a short last block with `valid` keys
+  auto consume = [&](auto mask_tag, const unsigned char* h0, const unsigned char* h1, int valid)
+                     __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s0[2], s1[2];
     uint32_t pb0[4][4], pb1[4][4];
     Soft st0, st1;
@@ -614,6 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
       if (i < 16) {
         s0[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 5], qf[ks], s0[mb], 0, 0, 0);
       } else {
+        if (MASK && i == 16) mask_missing_keys(s0, 0, h, valid);
         s1[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 5], qf[ks], s1[mb], 0, 0, 0);
         soft_piece(i - 16, s0, pb0, st0);
       }
@@ -623,6 +652,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
     // O^T += V0^T P0^T (operand reads two products ahead); softmax(S1) in its slots
     const unsigned char* v0 = h0 + kHalfBytes;
     const unsigned char* v1 = h1 + kHalfBytes;
+    if (MASK) mask_missing_keys(s1, 64, h, valid);
     bf16x8 va[3];
     va[0] = vread(v0, 0);
     va[1] = vread(v0, 1);
@@ -656,7 +686,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
     wait_copies_and_barrier();
     issue(2 * u + 3, slot(r0));
     issue(2 * u + 4, slot(r1));
-    if (myq >= 0 && (grp ? use_b : use_a)) consume(slot(s0), slot(s1));
+    if (myq >= 0 && (grp ? use_b : use_a)) consume(std::false_type{}, slot(s0), slot(s1), kBlock);
     return true;
   };
 
@@ -671,8 +701,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_pair_kernel(
     if (!step(u + 4, 3, 4, 1, 2)) break;
   }
 
+  // ---- the short last block, if selected: copied once all other copies have landed
+  if (short_a || short_b) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+    half_dma(sl0, k_rsrc, v_rsrc, last * kTileBytes, wave, lane);
+    half_dma(sl1, k_rsrc, v_rsrc, last * kTileBytes + kHalfBytes, wave, lane);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __syncthreads();
+    if (myq >= 0 && (grp ? short_b : short_a)) consume(std::true_type{}, sl0, sl1, L - last * kBlock);
+  }
+
   // ---- epilogue: O = O^T / l
-  if (myq < 0) return;
+  if (myq < 0 || qrow >= L) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
   unsigned char* op = out + head_off + (size_t)qrow * kD * 2;
@@ -694,7 +735,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, 
                            const int32_t* block_idx, const int32_t* qblock_order, float scale, void* out,
                            float* lse, hipStream_t stream) {
   (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
-  const int n_blocks = L / kBlock;
+  const int n_blocks = (L + kBlock - 1) / kBlock;   // the last block may be short
   const float scale_log2 = scale * 1.4426950408889634f;
   if (topk <= 64 * kListRegs) {
     const int n_pairs = (n_blocks + 1) / 2;

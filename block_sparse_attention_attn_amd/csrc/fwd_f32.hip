@@ -6,7 +6,8 @@
 // This path serves float32 inputs with small head dims; it is plain VALU code:
 // one thread per query row, the selected K/V block staged in LDS chunk by chunk
 // and read by every thread as a broadcast, an online (running-max) softmax in
-// float32 with accurate expf.
+// float32 with accurate expf.  A short last block (block does not divide L) has only
+// its remaining tokens, as queries and as keys.
 #include "launchers.h"
 
 namespace sol_attn {
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   const int i = qblock_order ? min(max(qblock_order[blockIdx.x], 0), n_blocks - 1) : (int)blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
-  const bool active = tid < block;
+  const bool active = tid < min(block, L - i * block);
   const size_t head = (size_t)bh * L * D;
   const size_t qrow = head + ((size_t)i * block + (active ? tid : 0)) * D;
 
@@ -43,8 +44,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   for (int t = 0; t < topk; ++t) {
     const int j = min(max(sel[t], 0), n_blocks - 1);
     const size_t kbase = head + (size_t)j * block * D;
-    for (int c0 = 0; c0 < block; c0 += kChunk) {
-      const int nc = min(kChunk, block - c0);
+    const int krows = min(block, L - j * block);
+    for (int c0 = 0; c0 < krows; c0 += kChunk) {
+      const int nc = min(kChunk, krows - c0);
       __syncthreads();
       for (int x = tid; x < nc * D; x += blockDim.x) {
         ks[x / D][x % D] = k[kbase + (size_t)c0 * D + x];
@@ -83,7 +85,7 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH
                           int block, int topk, const int32_t* block_idx, const int32_t* qblock_order,
                           float scale, float* out, float* lse, hipStream_t stream) {
   (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
-  const int n_blocks = L / block;
+  const int n_blocks = (L + block - 1) / block;
   dim3 grid(n_blocks, BH);
   const int threads = ((block + 63) / 64) * 64;
   if (d == 64)

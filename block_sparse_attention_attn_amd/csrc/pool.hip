@@ -3,7 +3,8 @@
 // Sol-Attn's preparation (the work done before the sparse attention proper) is
 // named as separately optimised in "Videomodel MiniMax-H3 rendert sneller dan
 // afspelen", section "Waar de snelheidswinst vandaan komt"; here it is the mean
-// of every contiguous block of `block` tokens, for Q and for K.
+// of every contiguous block of `block` tokens, for Q and for K.  When `block` does not
+// divide L the last block holds the remaining tokens and their mean is taken.
 //
 // HBM-bound: every input byte is read once with 16-byte loads (one row of a
 // block is covered by consecutive lanes, so a wave reads whole 256-byte rows),
@@ -42,12 +43,13 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
   for (int e = 0; e < kElemPerChunk; ++e) acc[e] = 0.0;
 
   const size_t row0 = (size_t)bh * L + (size_t)i * block;
+  const int rows = min(block, L - i * block);   // tokens in this block (fewer in a short last block)
   if (g < groups) {
     const u32x4* base = reinterpret_cast<const u32x4*>(
         static_cast<const char*>(src) + (row0 * d) * (kBf16 ? 2 : 4));
     const int row_chunks = chunks_per_row;
 #pragma unroll 4
-    for (int r = g; r < block; r += groups) {
+    for (int r = g; r < rows; r += groups) {
       const u32x4 x = __builtin_nontemporal_load(base + (size_t)r * row_chunks + c);
       if constexpr (kBf16) {
         const uint32_t w[4] = {x[0], x[1], x[2], x[3]};
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
   for (int e = tid; e < d; e += kThreads) {
     double s = 0.0;
     for (int gg = 0; gg < ng; ++gg) s += part[gg * d + e];
-    dst[((size_t)bh * n_blocks + i) * d + e] = s / (double)block;
+    dst[((size_t)bh * n_blocks + i) * d + e] = s / (double)rows;
   }
 }
 
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 hipError_t launch_pool(const void* q, const void* k, bool is_bf16, int BH, int L, int d, int block,
                        double* q_pooled, double* k_pooled, hipStream_t stream) {
   (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
-  const int n_blocks = L / block;
+  const int n_blocks = (L + block - 1) / block;
   const int chunks_per_row = d / (is_bf16 ? 8 : 4);
   const int groups = kThreads / chunks_per_row;
   const size_t lds = (size_t)groups * d * sizeof(double);

@@ -45,7 +45,6 @@ int check_common(int dtype, int B, int H, int L, int d, int block) {
     return fail(SOL_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (B < 0 || H < 0 || L < 0) return fail(SOL_ATTN_ERR_SHAPE, "negative size B=%d H=%d L=%d", B, H, L);
   if (d <= 0 || block <= 0) return fail(SOL_ATTN_ERR_SHAPE, "d=%d and block=%d must be positive", d, block);
-  if (L % block != 0) return fail(SOL_ATTN_ERR_SHAPE, "L=%d is not a multiple of block=%d", L, block);
   if ((long long)B * H > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "B*H too large");
   return SOL_ATTN_OK;
 }
@@ -63,7 +62,7 @@ int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, 
     return fail(SOL_ATTN_ERR_UNSUPPORTED, "pool needs d <= 512 and d %% %d == 0 (d=%d)", bf16 ? 8 : 4, d);
   const long long BH = (long long)B * H;
   if (BH * L == 0) return ok();
-  if (L / block > 0x7fffffff || BH > 65535)
+  if (BH > 65535)
     return fail(SOL_ATTN_ERR_SHAPE, "pool grid too large (B*H must be <= 65535)");
   if (!q || !k || !q_pooled || !k_pooled) return fail(SOL_ATTN_ERR_NULL, "pool: NULL pointer");
   if (!aligned(q, 16) || !aligned(k, 16)) return fail(SOL_ATTN_ERR_ALIGN, "pool: q/k not 16-byte aligned");
@@ -107,7 +106,7 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
                 block);
   const long long BH = (long long)B * H;
   if (BH * L == 0) return ok();
-  const int n_blocks = L / block;
+  const int n_blocks = (int)(((long long)L + block - 1) / block);   // the last block may be short
   if (topk < 1 || topk > n_blocks) return fail(SOL_ATTN_ERR_K, "topk=%d outside [1, n_blocks=%d]", topk, n_blocks);
   if (!bf16 && BH > 65535) return fail(SOL_ATTN_ERR_SHAPE, "fp32 fwd grid too large (B*H must be <= 65535)");
   if (!q || !k || !v || !block_idx || !out) return fail(SOL_ATTN_ERR_NULL, "fwd: NULL pointer");
@@ -130,11 +129,10 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
 }
 
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
-  if (block <= 0 || L < 0 || L % block != 0 || frame_tokens <= 0 || row_tokens <= 0 ||
-      row_tokens > frame_tokens)
+  if (block <= 0 || L < 0 || frame_tokens <= 0 || row_tokens <= 0 || row_tokens > frame_tokens)
     return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,
                 frame_tokens, row_tokens);
-  const int nb = L / block;
+  const int nb = (int)(((long long)L + block - 1) / block);
   if (nb > 0 && !order_host) return fail(SOL_ATTN_ERR_NULL, "frame_order: NULL output");
   std::vector<int32_t> idx(nb);
   for (int i = 0; i < nb; ++i) idx[i] = i;

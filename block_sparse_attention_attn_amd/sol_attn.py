@@ -6,7 +6,8 @@ passes raw device pointers plus the current HIP stream.  It never falls back to
 another implementation: if the library is missing, calls raise.
 
 Calls (same names as the C ABI):
-  sol_attn_pool(q, k, block)                         -> (q_pooled, k_pooled) float64 [B,H,L/block,d]
+  sol_attn_pool(q, k, block)                         -> (q_pooled, k_pooled) float64 [B,H,nB,d]
+                                                        (nB = ceil(L/block); a last block may be short)
   sol_attn_select(q_pooled, k_pooled, topk, ...)     -> block_idx int32 [B,H,nB,topk] (+ scores)
   sol_attn_fwd(q, k, v, block_idx, block, ...)       -> out [B,H,L,d] (+ lse float32 [B,H,L])
   sol_attn_frame_order(L, block, frame_tokens, row_tokens) -> int32 schedule of the query blocks
@@ -110,7 +111,7 @@ def sol_attn_pool(q: torch.Tensor, k: torch.Tensor, block: int) -> Tuple[torch.T
     lib = load_library()
     _check_qkv(q, k)
     B, H, L, d = q.shape
-    nb = L // block if block > 0 else 0
+    nb = -(-L // block) if block > 0 else 0
     qp = torch.empty((B, H, nb, d), dtype=torch.float64, device=q.device)
     kp = torch.empty_like(qp)
     _check("sol_attn_pool", lib.sol_attn_pool(_ptr(q), _ptr(k), _dtype_code(q), B, H, L, d, block,
@@ -135,7 +136,7 @@ def sol_attn_select(q_pooled: torch.Tensor, k_pooled: torch.Tensor, topk: int, r
 def sol_attn_frame_order(L: int, block: int, frame_tokens: int, row_tokens: int) -> torch.Tensor:
     """Host-computed query-block schedule for frame-major video tokens (int32 CPU tensor)."""
     lib = load_library()
-    nb = L // block if block > 0 else 0
+    nb = -(-L // block) if block > 0 else 0
     order = torch.empty(max(nb, 0), dtype=torch.int32)
     _check("sol_attn_frame_order", lib.sol_attn_frame_order(L, block, frame_tokens, row_tokens,
                                                             order.data_ptr() if nb else None))
@@ -160,14 +161,14 @@ def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: t
     if block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4:
         raise ValueError("block_idx must be contiguous int32 [B,H,nB,topk]")
     topk = block_idx.shape[-1]
-    if block > 0 and tuple(block_idx.shape[:3]) != (B, H, L // block):
+    if block > 0 and tuple(block_idx.shape[:3]) != (B, H, -(-L // block)):
         raise ValueError("block_idx leading dims must be [B,H,L/block]")
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
     if qblock_order is not None:
         if (qblock_order.dtype != torch.int32 or qblock_order.device != q.device or
-                qblock_order.numel() != (L // block if block > 0 else 0) or not qblock_order.is_contiguous()):
+                qblock_order.numel() != (-(-L // block) if block > 0 else 0) or not qblock_order.is_contiguous()):
             raise ValueError("qblock_order must be a contiguous int32 device tensor of L/block entries")
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
     _check("sol_attn_fwd", lib.sol_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, L, d, block, topk,

@@ -67,7 +67,7 @@ class Workload:
 
     @property
     def n_blocks(self) -> int:
-        return self.L // self.block
+        return -(-self.L // self.block)          # the last block may be short
 
     def effective_flops(self, topk: Optional[int] = None) -> float:
         """4*B*H*L*(k*Bs)*d: the two contractions over the selected key blocks."""

@@ -21,8 +21,8 @@
  *                    blocks only; no mask.
  *
  * Layout.  Q, K, V and O are contiguous [B, H, L, d] row-major (d fastest), in the
- * element type given by `dtype`.  Pooled tensors are [B, H, L/block, d] float64.
- * The block index list is int32 [B, H, L/block, topk], ascending per row.
+ * element type given by `dtype`.  Pooled tensors are [B, H, n_blocks, d] float64.
+ * The block index list is int32 [B, H, n_blocks, topk], ascending per row.
  *
  * Ownership and execution.  Every pointer argument is a DEVICE pointer owned by
  * the caller; the library allocates no memory, keeps no state between calls and
@@ -57,18 +57,24 @@ typedef enum {
 typedef enum {
   SOL_ATTN_OK = 0,
   SOL_ATTN_ERR_NULL = 1,        /* a required pointer is NULL                          */
-  SOL_ATTN_ERR_SHAPE = 2,       /* negative size, d/block <= 0, or L % block != 0      */
-  SOL_ATTN_ERR_K = 3,           /* topk < 1 or topk > L/block                          */
+  SOL_ATTN_ERR_SHAPE = 2,       /* negative size, or d/block <= 0                      */
+  SOL_ATTN_ERR_K = 3,           /* topk < 1 or topk > n_blocks                         */
   SOL_ATTN_ERR_UNSUPPORTED = 4, /* dtype / d / block combination not built (see calls) */
   SOL_ATTN_ERR_ALIGN = 5,       /* pointer not aligned as the call requires            */
   SOL_ATTN_ERR_HIP = 6          /* the HIP runtime rejected a launch                   */
 } sol_attn_status_t;
 
 /*
+ * Blocks: the sequence of L tokens is cut into n_blocks = ceil(L / block) contiguous
+ * blocks; block i holds tokens [i*block, min((i+1)*block, L)).  When block does not
+ * divide L the last block is short: its mean is over its own tokens, as a key block it
+ * contributes exactly those tokens, and as a query block only its existing rows are
+ * written.
+ *
  * Block mean-pooling of Q and K (the first half of the selection "preparation").
  *   q, k        [B,H,L,d] of `dtype`; 16-byte aligned.
- *   q_pooled,   [B,H,L/block,d] float64 outputs; 8-byte aligned.
- *   k_pooled    Element (b,h,i,e) = (sum over the block's rows of x[b,h,i*block+t,e]) / block.
+ *   q_pooled,   [B,H,n_blocks,d] float64 outputs; 8-byte aligned.
+ *   k_pooled    Element (b,h,i,e) = (sum over block i's rows of x[b,h,row,e]) / (its row count).
  *               The block sum is accumulated in float64 (exact whenever the block's
  *               values span less than ~2^35 in magnitude, so then order-independent);
  *               the division is IEEE-correctly rounded.
@@ -93,16 +99,16 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
 /*
  * Block-sparse exact softmax attention over the selected key blocks.
  *   q, k, v        [B,H,L,d] of `dtype`; 16-byte aligned.
- *   block_idx      int32 [B,H,L/block,topk]; every entry must lie in [0, L/block) and the
+ *   block_idx      int32 [B,H,n_blocks,topk]; every entry must lie in [0, n_blocks) and the
  *                  entries of a row must be distinct (sol_attn_select guarantees both).
  *                  Out-of-range entries are clamped into range instead of faulting; the
  *                  affected rows' results are then unspecified.
  *   qblock_order_or_null
- *                  optional int32 [L/block] device array: a permutation of the query blocks
+ *                  optional int32 [n_blocks] device array: a permutation of the query blocks
  *                  giving the order in which they are scheduled (shared by all (b,h)).
  *                  It changes only which blocks run concurrently -- and so how often K/V
  *                  tiles are re-read from cache rather than memory -- never the results.
- *                  NULL = ascending.  Entries outside [0, L/block) are clamped; a non-
+ *                  NULL = ascending.  Entries outside [0, n_blocks) are clamped; a non-
  *                  permutation leaves some output rows unwritten.  See sol_attn_frame_order.
  *   softmax_scale  multiplier of q.k inside the softmax; <= 0 selects 1/sqrt(d).
  *   out            [B,H,L,d] of `dtype`: O = softmax(q K_sel^T * scale) V_sel per query row;
@@ -123,8 +129,8 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
  * card, section "Usage").  Query blocks covering the same latent rows in different
  * frames select similar key blocks, so the order sorts blocks by (row of their first
  * token, frame, index): neighbouring entries then share K/V tiles in cache.
- *   order_host  HOST int32 [L/block] output (caller-owned).
- * Returns SOL_ATTN_ERR_SHAPE unless block > 0, L % block == 0, frame_tokens > 0 and
+ *   order_host  HOST int32 [n_blocks] output (caller-owned).
+ * Returns SOL_ATTN_ERR_SHAPE unless block > 0, L >= 0, frame_tokens > 0 and
  * 0 < row_tokens <= frame_tokens.
  */
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host);

@@ -42,7 +42,6 @@ def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, H=1, L=256, d=128, block=128
 def test_fwd_argument_errors(lib):
     assert _fwd(lib, dtype=7) == 4
     assert _fwd(lib, B=-1) == 2
-    assert _fwd(lib, L=200) == 2                       # not a multiple of block
     assert _fwd(lib, block=0) == 2
     assert _fwd(lib, d=64) == 4                        # bf16 path needs d = block = 128
     assert _fwd(lib, block=64, L=256) == 4
@@ -50,6 +49,7 @@ def test_fwd_argument_errors(lib):
     assert _fwd(lib, dtype=1, d=64, block=512, L=1024) == 4
     assert _fwd(lib, topk=0) == 3
     assert _fwd(lib, topk=3) == 3                      # only 2 blocks
+    assert _fwd(lib, L=200, topk=3) == 3               # 200 tokens: 2 blocks (the second short)
     assert _fwd(lib, q=None) == 1
     assert _fwd(lib, idx=None) == 1
     assert _fwd(lib, out=None) == 1
@@ -72,7 +72,7 @@ def test_pool_argument_errors(lib):
                                        kw.get("H", 1), kw.get("L", 256), kw.get("d", 128), kw.get("block", 128),
                                        kw.get("qp", FAKE), kw.get("kp", FAKE), None)
     assert p(dtype=3) == 4
-    assert p(L=100) == 2
+    assert p(L=-1) == 2
     assert p(d=12) == 4          # bf16 pool needs d % 8 == 0
     assert p(d=1024) == 4
     assert p(q=None) == 1
@@ -118,6 +118,7 @@ def test_frame_order(lib):
     frames = first // (48 * 84)
     keys = list(zip(rows, frames))
     assert keys == sorted(keys)
-    assert lib.sol_attn_frame_order(100, 32, 64, 32, None) == 2        # L % block
+    assert lib.sol_attn_frame_order(-1, 32, 64, 32, None) == 2         # negative L
+    assert S.sol_attn_frame_order(100, 32, 64, 32).numel() == 4        # a short last block counts
     assert lib.sol_attn_frame_order(128, 32, 64, 65, None) == 2        # row > frame
     assert lib.sol_attn_frame_order(0, 32, 64, 32, None) == 0          # empty
