@@ -7,5 +7,5 @@ it; the library's compute path never does, and the two share no code.
 """
 from .sol_attn_oracle import (  # noqa: F401
     widen, n_blocks, block_rows, pool, block_scores, select, select_from_scores, attend, attend_block,
-    selection_margins, run, window_selection,
+    selection_margins, run, window_selection, cube_blocks, pool_sets, attend_sets, run_cube,
 )

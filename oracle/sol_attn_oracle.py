@@ -23,6 +23,10 @@ The concrete reading implemented (the pages give no formula)
 * every query of block i then attends with exact softmax(q k^T / sqrt(d)) over
   the union of the selected key blocks' tokens, with no mask.
 
+Second blocking (cube_blocks, run_cube): on a T x h x w latent grid a block may be
+a bt x by x bx box of latents instead of a run of consecutive tokens; pooling,
+selection and attention are then the same definitions over those token sets.
+
 Ranking uses the unscaled r_ij: multiplying by the positive constant 1/sqrt(d)
 preserves the order in exact arithmetic, and not applying it avoids creating
 rounding ties.  Everything is float64; inputs are the exact widenings of the
@@ -39,7 +43,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["widen", "n_blocks", "block_rows", "pool", "block_scores", "select", "select_from_scores",
-           "attend", "attend_block", "selection_margins", "run", "window_selection"]
+           "attend", "attend_block", "selection_margins", "run", "window_selection",
+           "cube_blocks", "pool_sets", "attend_sets", "run_cube"]
 
 
 def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
@@ -116,12 +121,14 @@ def attend_block(Qi: np.ndarray, K: np.ndarray, V: np.ndarray, sel_i: np.ndarray
     Qi [rows of the block, d]; K, V [L, d] of the same (b, h); sel_i [k] key-block indices.
     Returns (O_i [Bs, d], lse_i [Bs]) with lse = m + ln(sum exp(z - m)).
     """
-    d = K.shape[-1]
     rows = (sel_i[:, None] * block + np.arange(block)[None, :]).reshape(-1)
     rows = rows[rows < K.shape[0]]           # a short last block has only its own tokens
-    Kc = K[rows]
-    Vc = V[rows]
-    z = (Qi @ Kc.T) * scale                  # [Bs, k*Bs]
+    return _softmax_attend(Qi, K[rows], V[rows], scale)
+
+
+def _softmax_attend(Qi: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, scale: float):
+    """softmax(Qi Kc^T * scale) Vc and its log-sum-exp, for query rows Qi and key/value rows Kc, Vc."""
+    z = (Qi @ Kc.T) * scale                  # [rows, keys]
     m = z.max(axis=1, keepdims=True)
     p = np.exp(z - m)
     l = p.sum(axis=1, keepdims=True)
@@ -170,6 +177,72 @@ def window_selection(n_blocks: int, topk: int) -> np.ndarray:
         s = starts[np.flatnonzero(dist == dist.min())[-1]]
         out[i] = np.arange(s, s + topk)
     return out
+
+
+def cube_blocks(T: int, h: int, w: int, cube) -> np.ndarray:
+    """3-D blocking of a T x h x w latent token grid (the latent of a clip is frames x
+    rows x cols, Sol-H3-VAE model card, section "Usage"; token n = (t*h + y)*w + x).
+
+    Reading: a block is a box of bt x by x bx latents (cube = (bt, by, bx)), which must
+    divide (T, h, w); boxes are numbered like the tokens themselves (time slowest, then
+    row, then column), and inside a box its tokens keep their frame-major order.
+    Returns int64 [nB, bt*by*bx]: row i lists the token indices of block i."""
+    bt, by, bx = cube
+    if min(bt, by, bx) < 1 or T % bt or h % by or w % bx:
+        raise ValueError("cube does not tile the latent grid")
+    blocks = []
+    for tc in range(T // bt):
+        for yc in range(h // by):
+            for xc in range(w // bx):
+                blocks.append([(t * h + y) * w + x
+                               for t in range(tc * bt, (tc + 1) * bt)
+                               for y in range(yc * by, (yc + 1) * by)
+                               for x in range(xc * bx, (xc + 1) * bx)])
+    return np.asarray(blocks, dtype=np.int64).reshape(-1, bt * by * bx)
+
+
+def pool_sets(X: np.ndarray, sets: np.ndarray) -> np.ndarray:
+    """Block mean over arbitrary token sets: [..., L, d] -> [..., nB, d], block i = mean of X[..., sets[i], :]."""
+    *lead, L, d = X.shape
+    out = np.empty((*lead, sets.shape[0], d), dtype=np.float64)
+    for i, rows in enumerate(sets):
+        out[..., i, :] = X[..., rows, :].sum(axis=-2) / len(rows)
+    return out
+
+
+def attend_sets(Q: np.ndarray, K: np.ndarray, V: np.ndarray, sets: np.ndarray, sel: np.ndarray,
+                scale: Optional[float] = None, qblocks: Optional[np.ndarray] = None):
+    """Block-sparse attention with blocks given as token sets: the rows sets[i] of query
+    block i attend over the tokens of the key blocks sel[..., i, :].  Inputs and outputs
+    keep the token order of Q (for cube blocks: frame-major).  Other arguments as attend()."""
+    *lead, L, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nb = sets.shape[0]
+    Qf, Kf, Vf = (x.reshape(-1, L, d) for x in (Q, K, V))
+    sf = sel.reshape(-1, nb, sel.shape[-1])
+    O = np.full(Qf.shape, np.nan)
+    lse = np.full(Qf.shape[:2], np.nan)
+    blocks = range(nb) if qblocks is None else qblocks
+    for bh in range(Qf.shape[0]):
+        for i in blocks:
+            rows = sets[i]
+            keys = sets[sf[bh, i]].reshape(-1)
+            O[bh, rows], lse[bh, rows] = _softmax_attend(Qf[bh, rows], Kf[bh, keys], Vf[bh, keys], scale)
+    return O.reshape(*lead, L, d), lse.reshape(*lead, L)
+
+
+def run_cube(q_stored, k_stored, v_stored, dtype: str, grid, cube, topk: int,
+             qblocks: Optional[np.ndarray] = None):
+    """Whole path with 3-D cube blocks on stored frame-major inputs [B,H,L,d], L = T*h*w:
+    returns dict(sets, qbar, kbar, idx, out, lse); idx indexes cubes, out/lse are frame-major."""
+    T, h, w = grid
+    sets = cube_blocks(T, h, w, cube)
+    Q, K, V = widen(q_stored, dtype), widen(k_stored, dtype), widen(v_stored, dtype)
+    qbar, kbar = pool_sets(Q, sets), pool_sets(K, sets)
+    idx = select(qbar, kbar, topk)
+    out, lse = attend_sets(Q, K, V, sets, idx, qblocks=qblocks)
+    return dict(sets=sets, qbar=qbar, kbar=kbar, idx=idx, out=out, lse=lse)
 
 
 def selection_margins(Qbar: np.ndarray, Kbar: np.ndarray, topk: int):
