@@ -42,9 +42,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="refine_1344x768")
     p.add_argument("--topk", type=int, default=None, help="override k (e.g. all blocks for a dense run)")
-    p.add_argument("--pattern", choices=["selected", "window"], default="selected",
+    p.add_argument("--pattern", choices=["selected", "window", "cube"], default="selected",
                    help="selected: pool -> select -> fwd (the method); window: fwd alone with the static "
-                        "window pattern of sol_attn_window_blocks (same k)")
+                        "window pattern of sol_attn_window_blocks (same k); cube: the method with 3-D "
+                        "cube blocks (tokens reordered to cube-major order, the path, outputs reordered back)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="after timing, run one plain device copy of Q (size known) to calibrate traffic counters")
@@ -67,7 +68,11 @@ def cpu_baseline(wl, q, k, v, topk, n_heads, pattern="selected"):
     ks = k.reshape(-1, wl.L, wl.d)[:n_heads]
     vs = v.reshape(-1, wl.L, wl.d)[:n_heads]
     t0 = time.perf_counter()
-    if pattern == "window":
+    if pattern == "cube":
+        oracle.run_cube(qs, ks, vs, wl.dtype, wl.grid, wl.cube, topk)
+        what = (f"whole path with {'x'.join(map(str, wl.cube))} cube blocks (pool, scores, top-{topk}, float64 "
+                f"attention of all {wl.n_blocks} query boxes)")
+    elif pattern == "window":
         sel = np.broadcast_to(oracle.window_selection(wl.n_blocks, topk), (n_heads, wl.n_blocks, topk))
         oracle.attend(oracle.widen(qs, wl.dtype), oracle.widen(ks, wl.dtype), oracle.widen(vs, wl.dtype), sel,
                       wl.block)
@@ -119,34 +124,59 @@ def main():
     s_ptr = stream.cuda_stream
 
     window = args.pattern == "window"
+    cube = args.pattern == "cube"
     if window:
         idx.copy_(S.sol_attn_window_blocks(nb, topk).view(1, 1, nb, topk).expand(wl.B, wl.H, nb, topk))
+    T, h, w = wl.grid
+    bt, by, bx = wl.cube
+    if cube:
+        # boxes of bt x by x bx latents: tokens reordered to cube-major order, blocks of one box
+        if bt * by * bx != wl.block:
+            raise SystemExit(f"cube {wl.cube} does not hold one block of {wl.block} tokens")
+        Qc, Kc, Vc, Oc = (torch.empty_like(Q) for _ in range(4))
+        ny, nx = h // by, w // bx
+        order = S.sol_attn_frame_order(wl.L, wl.block, wl.block * ny * nx, wl.block * nx).cuda()
+    else:
+        Qc, Kc, Vc, Oc = Q, K, V, out
+    row_bytes = wl.d * Q.element_size()
 
-    def step(ev=None):
-        if window:   # static pattern: the step is the attention alone
-            for e in (ev or [])[:3]:
-                e.record(stream)
-            S._check("fwd", lib.sol_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dtc, wl.B, wl.H, wl.L,
-                                             wl.d, wl.block, topk, idx.data_ptr(), order.data_ptr(), 0.0,
-                                             out.data_ptr(), None, s_ptr))
-            if ev is not None:
-                ev[3].record(stream)
-            return
-        if ev is not None:
-            ev[0].record(stream)
-        S._check("pool", lib.sol_attn_pool(Q.data_ptr(), K.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d, wl.block,
+    def permute(src, dst, inverse):
+        S._check("cube_permute", lib.sol_attn_cube_permute(src.data_ptr(), dst.data_ptr(), wl.B, wl.H, T, h, w,
+                                                           row_bytes, bt, by, bx, int(inverse), s_ptr))
+
+    def run_pool():
+        S._check("pool", lib.sol_attn_pool(Qc.data_ptr(), Kc.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d, wl.block,
                                            qp.data_ptr(), kp.data_ptr(), s_ptr))
-        if ev is not None:
-            ev[1].record(stream)
+
+    def run_select():
         S._check("select", lib.sol_attn_select(qp.data_ptr(), kp.data_ptr(), wl.B, wl.H, nb, wl.d, topk,
                                                idx.data_ptr(), None, s_ptr))
-        if ev is not None:
-            ev[2].record(stream)
-        S._check("fwd", lib.sol_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d,
-                                         wl.block, topk, idx.data_ptr(), order.data_ptr(), 0.0, out.data_ptr(),
+
+    def run_fwd():
+        S._check("fwd", lib.sol_attn_fwd(Qc.data_ptr(), Kc.data_ptr(), Vc.data_ptr(), dtc, wl.B, wl.H, wl.L, wl.d,
+                                         wl.block, topk, idx.data_ptr(), order.data_ptr(), 0.0, Oc.data_ptr(),
                                          None, s_ptr))
+
+    def run_permute_in():
+        for src, dst in ((Q, Qc), (K, Kc), (V, Vc)):
+            permute(src, dst, False)
+
+    # the phases of one step, timed one by one in a separate pass
+    if window:      # static pattern: the step is the attention alone
+        phases = [("fwd", run_fwd)]
+    elif cube:
+        phases = [("permute_in", run_permute_in), ("pool", run_pool), ("select", run_select), ("fwd", run_fwd),
+                  ("permute_out", lambda: permute(Oc, out, True))]
+    else:
+        phases = [("pool", run_pool), ("select", run_select), ("fwd", run_fwd)]
+
+    def step(ev=None):
+        for n, (_, fn) in enumerate(phases):
+            if ev is not None:
+                ev[n].record(stream)
+            fn()
         if ev is not None:
-            ev[3].record(stream)
+            ev[len(phases)].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -164,13 +194,12 @@ def main():
     ms_per_step = start.elapsed_time(stop) / args.steps
 
     # per-kernel durations (separate pass, events between the three launches)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    t_pool = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    t_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    t_fwd = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    t_phase = {name: float(np.mean([e[n].elapsed_time(e[n + 1]) for e in evs])) for n, (name, _) in enumerate(phases)}
+    t_pool, t_fwd = t_phase.get("pool"), t_phase["fwd"]
 
     if args.copy_probe:
         out.copy_(Q)
@@ -193,17 +222,21 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded smooth field + noise, unit RMS)",
-        "config": {"workload": wl.name + ("+window" if window else ""), "B": wl.B, "H": wl.H, "L": wl.L,
-                   "d": wl.d, "block": wl.block, "topk": topk, "n_blocks": nb,
-                   "latent": [wl.frames, wl.lat_h, wl.lat_w], "pattern": args.pattern},
+        "config": {"workload": wl.name + ("+" + args.pattern if args.pattern != "selected" else ""), "B": wl.B,
+                   "H": wl.H, "L": wl.L, "d": wl.d, "block": wl.block, "topk": topk, "n_blocks": nb,
+                   "latent": [wl.frames, wl.lat_h, wl.lat_w], "pattern": args.pattern,
+                   **({"cube": list(wl.cube)} if cube else {})},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "kernels_ms": {"pool": round(t_pool, 4), "select": round(t_sel, 4), "fwd": round(t_fwd, 4)},
+        "kernels_ms": {name: round(t, 4) for name, t in t_phase.items()},
         "fwd_tflops": round(fwd_tflops, 2),
-        "pool_gbs": None if window else round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
+        "pool_gbs": None if t_pool is None else round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": FWD_TRAFFIC_BYTES if (wl.name == "refine_1344x768" and topk == wl.topk
-                                                      and not window) else None},
+                                                      and args.pattern == "selected") else None},
+        **({"permute_gbs": round(4 * 2 * wl.B * wl.H * wl.L * row_bytes
+                                 / ((t_phase["permute_in"] + t_phase["permute_out"]) * 1e-3) / 1e9, 1)}
+           if cube else {}),
         "timed_wall_s": round(wall, 3),
         "input_gen_s": round(t_gen, 2),
     }

@@ -23,4 +23,8 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH
                           int block, int topk, const int32_t* block_idx, const int32_t* qblock_order,
                           float scale, float* out, float* lse, hipStream_t stream);
 
+// Token rows between frame-major and cube-major order (3-D cube blocks).
+hipError_t launch_cube_permute(const void* src, void* dst, int BH, int T, int h, int w, int row_bytes, int bt,
+                               int by, int bx, bool inverse, hipStream_t stream);
+
 }  // namespace sol_attn

@@ -128,6 +128,30 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
                     "fwd fp32 launch");
 }
 
+int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
+                          int by, int bx, int inverse, void* stream) {
+  if (B < 0 || H < 0 || T < 0 || h < 0 || w < 0)
+    return fail(SOL_ATTN_ERR_SHAPE, "cube_permute: negative size B=%d H=%d T=%d h=%d w=%d", B, H, T, h, w);
+  if (row_bytes <= 0 || row_bytes % 4 != 0)
+    return fail(SOL_ATTN_ERR_SHAPE, "cube_permute: row_bytes=%d must be a positive multiple of 4", row_bytes);
+  if (bt < 1 || by < 1 || bx < 1 || T % bt || h % by || w % bx)
+    return fail(SOL_ATTN_ERR_SHAPE, "cube_permute: box %dx%dx%d does not tile the %dx%dx%d grid", bt, by, bx, T, h,
+                w);
+  if (inverse != 0 && inverse != 1) return fail(SOL_ATTN_ERR_SHAPE, "cube_permute: inverse must be 0 or 1");
+  const long long BH = (long long)B * H;
+  const long long L = (long long)T * h * w;
+  if (BH * L == 0) return ok();
+  if (BH > 65535) return fail(SOL_ATTN_ERR_SHAPE, "cube_permute grid too large (B*H must be <= 65535)");
+  if (L > 0x7fffffffLL || (long long)bt * by * bx * row_bytes > (1LL << 32))
+    return fail(SOL_ATTN_ERR_SHAPE, "cube_permute: grid of %lld tokens or box of %lld bytes too large", L,
+                (long long)bt * by * bx * row_bytes);
+  if (!src || !dst) return fail(SOL_ATTN_ERR_NULL, "cube_permute: NULL pointer");
+  if (!aligned(src, 4) || !aligned(dst, 4)) return fail(SOL_ATTN_ERR_ALIGN, "cube_permute: src/dst not 4-byte aligned");
+  return hip_status(sol_attn::launch_cube_permute(src, dst, (int)BH, T, h, w, row_bytes, bt, by, bx, inverse == 1,
+                                                  static_cast<hipStream_t>(stream)),
+                    "cube_permute launch");
+}
+
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
   if (block <= 0 || L < 0 || frame_tokens <= 0 || row_tokens <= 0 || row_tokens > frame_tokens)
     return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,

@@ -12,7 +12,9 @@ Calls (same names as the C ABI):
   sol_attn_fwd(q, k, v, block_idx, block, ...)       -> out [B,H,L,d] (+ lse float32 [B,H,L])
   sol_attn_frame_order(L, block, frame_tokens, row_tokens) -> int32 schedule of the query blocks
   sol_attn_window_blocks(n_blocks, topk)             -> int32 [n_blocks, topk] static window pattern
+  sol_attn_cube_permute(x, grid, cube, inverse)      -> x with its tokens in cube-major (or frame-major) order
   sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
+  cube_sparse_attention(q, k, v, grid, cube, topk)   -> the same with 3-D cube blocks
 """
 from __future__ import annotations
 
@@ -58,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_frame_order.restype = i
     lib.sol_attn_window_blocks.argtypes = [i, i, vp]
     lib.sol_attn_window_blocks.restype = i
+    lib.sol_attn_cube_permute.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, i, vp]
+    lib.sol_attn_cube_permute.restype = i
     lib.sol_attn_last_error.argtypes = []
     lib.sol_attn_last_error.restype = ctypes.c_char_p
     lib.sol_attn_version.argtypes = []
@@ -185,6 +189,51 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: i
     qp, kp = sol_attn_pool(q, k, block)
     idx = sol_attn_select(qp, kp, topk)
     return sol_attn_fwd(q, k, v, idx, block, softmax_scale, return_lse, qblock_order=qblock_order)
+
+
+def sol_attn_cube_permute(x: torch.Tensor, grid: Tuple[int, int, int], cube: Tuple[int, int, int],
+                          inverse: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reorder the tokens of x ([B,H,L,d] or [B,H,L], L = T*h*w for grid = (T,h,w)) from
+    frame-major to cube-major order for boxes cube = (bt,by,bx), or back with inverse=True."""
+    lib = load_library()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() not in (3, 4):
+        raise ValueError("x must be a contiguous device tensor [B,H,L,d] or [B,H,L]")
+    B, H, L = x.shape[:3]
+    T, h, w = grid
+    if T * h * w != L:
+        raise ValueError(f"grid {grid} does not hold L={L} tokens")
+    row_bytes = (x.shape[3] if x.dim() == 4 else 1) * x.element_size()
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must match x")
+    bt, by, bx = cube
+    _check("sol_attn_cube_permute", lib.sol_attn_cube_permute(_ptr(x), _ptr(out), B, H, T, h, w, row_bytes, bt, by,
+                                                              bx, int(bool(inverse)), _stream(x)))
+    return out
+
+
+def cube_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Tuple[int, int, int],
+                          cube: Tuple[int, int, int], topk: int, softmax_scale: Optional[float] = None,
+                          return_lse: bool = False, return_idx: bool = False):
+    """Sparse attention with 3-D cube blocks on frame-major q, k, v: reorder to cube-major,
+    pool -> select -> fwd with block = bt*by*bx, reorder the outputs back.  block_idx (if
+    returned) indexes boxes in cube-major numbering."""
+    T, h, w = grid
+    bt, by, bx = cube
+    V = bt * by * bx
+    qc, kc, vc = (sol_attn_cube_permute(x, grid, cube) for x in (q, k, v))
+    qp, kp = sol_attn_pool(qc, kc, V)
+    idx = sol_attn_select(qp, kp, topk)
+    order = sol_attn_frame_order(q.shape[2], V, V * (h // by) * (w // bx), V * (w // bx)).to(q.device)
+    res = sol_attn_fwd(qc, kc, vc, idx, V, softmax_scale, return_lse, qblock_order=order)
+    oc, lc = res if return_lse else (res, None)
+    out = [sol_attn_cube_permute(oc, grid, cube, inverse=True)]
+    if return_lse:
+        out.append(sol_attn_cube_permute(lc, grid, cube, inverse=True))
+    if return_idx:
+        out.append(idx)
+    return out[0] if len(out) == 1 else tuple(out)
 
 
 def version() -> int:

@@ -60,6 +60,11 @@ class Workload:
     unit_rms: bool
     seed: int
     extra_topk: Tuple[int, ...] = ()   # further k values run on the same tensors
+    cube: Tuple[int, int, int] = (1, 1, 1)   # (bt, by, bx) box for 3-D cube blocks, bt*by*bx == block
+
+    @property
+    def grid(self) -> Tuple[int, int, int]:
+        return (self.frames, self.lat_h, self.lat_w)
 
     @property
     def L(self) -> int:
@@ -78,15 +83,20 @@ class Workload:
 # The five workloads: a tiny fp32 case the oracle finishes instantly, the
 # 896x512 draft stage, the 1344x768 refinement stage (the headline size,
 # 64,512 tokens), a 10 s clip at 1344x768 and a 2K (2048x1152) refinement.
+# `cube` is the box used when the same tokens are cut into 3-D blocks: one block's
+# worth of latents (bt*by*bx == block) that tiles the grid -- 2x8x8 where 8 divides
+# the latent width, 4x8x4 at 1344x768, whose 84 latent columns 8 does not divide.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in [
         Workload("tiny_fp32_1k", 1, 2, 64, "fp32", 4, 16, 16, 64, 4, (2, 4, 4), False, 0,
-                 extra_topk=(16,)),
-        Workload("draft_896x512", 1, 40, 128, "bf16", 16, 32, 56, 128, 56, (4, 8, 14), True, 1),
-        Workload("refine_1344x768", 1, 40, 128, "bf16", 16, 48, 84, 128, 76, (4, 12, 21), True, 2),
-        Workload("clip10s_1344x768", 1, 40, 128, "bf16", 32, 48, 84, 128, 101, (8, 12, 21), True, 3),
+                 extra_topk=(16,), cube=(4, 4, 4)),
+        Workload("draft_896x512", 1, 40, 128, "bf16", 16, 32, 56, 128, 56, (4, 8, 14), True, 1, cube=(2, 8, 8)),
+        Workload("refine_1344x768", 1, 40, 128, "bf16", 16, 48, 84, 128, 76, (4, 12, 21), True, 2,
+                 cube=(4, 8, 4)),
+        Workload("clip10s_1344x768", 1, 40, 128, "bf16", 32, 48, 84, 128, 101, (8, 12, 21), True, 3,
+                 cube=(4, 8, 4)),
         Workload("refine_2k", 1, 40, 128, "bf16", 16, 72, 128, 128, 92, (4, 18, 32), True, 4,
-                 extra_topk=(1152,)),
+                 extra_topk=(1152,), cube=(2, 8, 8)),
     ]
 }
 HEADLINE = "refine_1344x768"

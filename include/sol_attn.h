@@ -151,6 +151,30 @@ int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int
  */
 int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
 
+/*
+ * Token reordering for 3-D cube blocks (device copy).  The tokens of a clip form a
+ * T x h x w latent grid (frames x rows x cols; Sol-H3-VAE model card, section "Usage"),
+ * stored frame-major: token n = (t*h + y)*w + x.  A cube block is a bt x by x bx box of
+ * that grid.  Cube-major order numbers the boxes like the tokens (time slowest, then
+ * row, then column) and keeps the frame-major order of the tokens inside a box, so box
+ * c is tokens [c*V, (c+1)*V) of the reordered sequence, V = bt*by*bx.  Pooling, scoring
+ * and softmax only see token sets, so block-sparse attention with cube blocks is:
+ *   1. cube_permute Q, K, V (inverse = 0);
+ *   2. sol_attn_pool / sol_attn_select / sol_attn_fwd with block = V on the reordered
+ *      tensors (block_idx then indexes boxes);
+ *   3. cube_permute O (and lse, with row_bytes = 4) back with inverse = 1.
+ * A model whose token-wise layers do not care about order can keep its activations in
+ * cube-major order and skip steps 1 and 3.
+ *   src, dst    [B,H,T*h*w] rows of row_bytes bytes each (a [B,H,L,d] tensor has
+ *               row_bytes = d * element size); must not overlap; 4-byte aligned (16-byte
+ *               alignment and bx*row_bytes % 16 == 0 select 16-byte accesses).
+ *   inverse     0: dst row p = src row n(p) (frame-major -> cube-major); 1: the reverse.
+ * Returns SOL_ATTN_ERR_SHAPE for negative sizes, row_bytes not a positive multiple of 4,
+ * a box that does not divide the grid (no partial boxes), inverse not 0/1, or B*H > 65535.
+ */
+int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
+                          int by, int bx, int inverse, void* stream);
+
 /* Human-readable description of the last failure on the calling thread ("" if none). */
 const char* sol_attn_last_error(void);
 

@@ -20,7 +20,8 @@ def lib():
 def test_header_symbols_exported(lib):
     names = S.header_symbols()
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
-                          "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks"}
+                          "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks",
+                          "sol_attn_cube_permute"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -122,3 +123,23 @@ def test_frame_order(lib):
     assert S.sol_attn_frame_order(100, 32, 64, 32).numel() == 4        # a short last block counts
     assert lib.sol_attn_frame_order(128, 32, 64, 65, None) == 2        # row > frame
     assert lib.sol_attn_frame_order(0, 32, 64, 32, None) == 0          # empty
+
+
+def _perm(lib, src=FAKE, dst=FAKE + 0x100000, B=1, H=1, T=4, h=8, w=8, row_bytes=256, bt=2, by=4, bx=4, inv=0):
+    return lib.sol_attn_cube_permute(src, dst, B, H, T, h, w, row_bytes, bt, by, bx, inv, None)
+
+
+def test_cube_permute_argument_checks(lib):
+    assert _perm(lib, T=-1) == 2                       # negative size
+    assert _perm(lib, row_bytes=0) == 2                # empty rows
+    assert _perm(lib, row_bytes=6) == 2                # not a multiple of 4
+    assert _perm(lib, bt=3) == 2                       # box does not divide T
+    assert _perm(lib, by=3) == 2                       # ... h
+    assert _perm(lib, bx=0) == 2                       # ... w
+    assert _perm(lib, inv=2) == 2
+    assert _perm(lib, B=65536) == 2                    # grid.y limit
+    assert _perm(lib, src=None) == 1
+    assert _perm(lib, dst=MIS) == 5
+    assert _perm(lib, H=0, src=None) == 0              # nothing to do
+    assert _perm(lib, T=0, h=0, w=0) == 0
+    assert b"does not tile" in (_perm(lib, by=3), lib.sol_attn_last_error())[1]

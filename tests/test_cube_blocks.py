@@ -139,3 +139,113 @@ def test_cube_selection_follows_the_box_means():
         Q[rows, i] = 1.0
     idx = oracle.select(oracle.pool_sets(Q, sets), oracle.pool_sets(K, sets), 1)
     assert np.array_equal(idx[:, 0], np.arange(8))
+
+
+# ----------------------------------------------------------------------------- GPU
+def _gpu_lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_attention_attn_amd import sol_attn
+    sol_attn.load_library()
+    return sol_attn
+
+
+def _dev(x, dtype):
+    x = np.ascontiguousarray(x)
+    if dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape,grid,cube,dtype", [
+    ((1, 3, 1024, 128), (4, 16, 16), (2, 8, 8), torch.bfloat16),      # 16-byte units, 2 KiB runs
+    ((2, 2, 64512, 128), (16, 48, 84), (4, 8, 4), torch.bfloat16),    # 1344x768 grid, 1 KiB runs
+    ((1, 2, 1024, 64), (4, 16, 16), (4, 4, 4), torch.float32),
+    ((1, 2, 360), (3, 10, 12), (3, 2, 3), torch.float32),             # lse-like rows of 4 bytes
+    ((2, 1, 240, 3), (4, 6, 10), (2, 3, 5), torch.float32),           # 12-byte rows, 4-byte units
+    ((1, 1, 240, 3), (4, 6, 10), (1, 2, 2), torch.float32),            # 24-byte runs, 4-byte units
+])
+def test_cube_permute_is_the_oracle_order(shape, grid, cube, dtype):
+    """Pure data movement: bit-exact against gathering by the oracle's token sets, and
+    the inverse restores the original bits."""
+    S = _gpu_lib()
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(shape, generator=g).to(dtype)
+    sets = oracle.cube_blocks(*grid, cube).reshape(-1)
+    want = x[:, :, torch.from_numpy(sets)]
+    xd = x.cuda()
+    y = S.sol_attn_cube_permute(xd, grid, cube)
+    back = S.sol_attn_cube_permute(y, grid, cube, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       want.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+    assert torch.equal(back.cpu(), x)
+
+
+def _check_cube_path(S, q, k, v, dtype, grid, cube, topk, scale_tol):
+    ref = oracle.run_cube(q, k, v, dtype, grid, cube, topk)
+    Q, K, V = _dev(q, dtype), _dev(k, dtype), _dev(v, dtype)
+    out, lse, idx = S.cube_sparse_attention(Q, K, V, grid, cube, topk, return_lse=True, return_idx=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"]), "selection differs from the oracle"
+    err = np.abs(out.double().cpu().numpy() - ref["out"])
+    lerr = np.abs(lse.double().cpu().numpy() - ref["lse"])
+    if dtype == "bf16":
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+        assert lerr.max() <= 1e-2
+    else:
+        assert err.max() <= scale_tol and lerr.max() <= scale_tol, (err.max(), lerr.max())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("topk", [1, 3, 8])
+def test_cube_path_bf16_matches_oracle(topk):
+    import dataclasses
+    from block_sparse_attention_attn_amd import workloads as W
+    S = _gpu_lib()
+    wl = dataclasses.replace(W.get("draft_896x512"), name="cube", H=2, frames=4, lat_h=16, lat_w=16,
+                             coarse=(2, 4, 4), topk=topk, seed=31, cube=(2, 8, 8))      # 8 boxes of 128
+    q, k, v = W.make_qkv(wl)
+    _check_cube_path(S, q, k, v, "bf16", wl.grid, wl.cube, topk, None)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("topk", [4, 16])
+def test_cube_path_fp32_tiny_workload(topk):
+    from block_sparse_attention_attn_amd import workloads as W
+    S = _gpu_lib()
+    wl = W.get("tiny_fp32_1k")
+    q, k, v = W.make_qkv(wl)
+    _check_cube_path(S, q, k, v, "fp32", wl.grid, wl.cube, topk, 1e-5)
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_cube_path_full_size():
+    """1344x768 workload (64,512 tokens, 40 heads) cut into 4x8x4 boxes, k = 76: the
+    whole selection bit-exact, outputs on sampled query boxes of sampled heads."""
+    from block_sparse_attention_attn_amd import workloads as W
+    S = _gpu_lib()
+    wl = W.get("refine_1344x768")
+    q, k, v = W.make_qkv(wl)
+    sets = oracle.cube_blocks(*wl.grid, wl.cube)
+    Q, K, V = _dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16")
+    out, idx = S.cube_sparse_attention(Q, K, V, wl.grid, wl.cube, wl.topk, return_idx=True)
+    torch.cuda.synchronize()
+    Qd, Kd, Vd = (oracle.widen(x, "bf16") for x in (q, k, v))
+    want_idx = oracle.select(oracle.pool_sets(Qd, sets), oracle.pool_sets(Kd, sets), wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    nb = sets.shape[0]
+    o = out.view(-1, wl.L, wl.d)
+    Qd, Kd, Vd = (x.reshape(-1, wl.L, wl.d) for x in (Qd, Kd, Vd))
+    rng = np.random.default_rng(7)
+    errs = []
+    sel = want_idx.reshape(-1, nb, wl.topk)
+    for bh in rng.choice(wl.B * wl.H, 3, replace=False):
+        blocks = [0, nb - 1] + list(rng.choice(nb, 2, replace=False))
+        Oh, _ = oracle.attend_sets(Qd[bh], Kd[bh], Vd[bh], sets, sel[bh], qblocks=blocks)
+        rows = sets[blocks].reshape(-1)
+        errs.append(np.abs(o[bh, torch.from_numpy(rows)].double().cpu().numpy() - Oh[rows]))
+    err = np.concatenate(errs)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())

@@ -74,3 +74,10 @@ def test_draft_workload_unit_rms_and_bf16():
     a = v[0, 0, :-1, 0]
     b = v[0, 0, 1:, 0]
     assert np.corrcoef(a, b)[0, 1] > 0.5
+
+
+def test_cube_boxes_tile_the_grid():
+    for wl in W.WORKLOADS.values():
+        (T, h, w), (bt, by, bx) = wl.grid, wl.cube
+        assert T % bt == 0 and h % by == 0 and w % bx == 0, wl.name
+        assert bt * by * bx == wl.block, wl.name
