@@ -9,3 +9,4 @@ from .sol_attn_oracle import (  # noqa: F401
     widen, n_blocks, block_rows, pool, block_scores, select, select_from_scores, attend, attend_block,
     selection_margins, run, window_selection, cube_blocks, pool_sets, attend_sets, run_cube,
 )
+from . import quant_oracle  # noqa: F401,E402
