@@ -13,11 +13,14 @@ The reading implemented
   With d = 128 a row then costs d + 4 = 132 bytes against 2d = 256 in bf16: 51.56 %
   of the bf16 bytes, the page's figure read as the size that remains (a cut *by*
   51.6 % would leave less than one byte per value, which 8-bit codes cannot reach).
-* INT8 (Q, K, V): scale = amax / 127 with amax = max |x| over the row;
-  code = round-half-even(x / scale), clamped to [-127, 127].
+* INT8 (Q, K, V): with amax = max |x| over the row, the stored scale is amax / 127 and
+  code = round-half-even(x * (127 / amax)), clamped to [-127, 127].
 * FP8 (the output): OCP E4M3 ("e4m3fn": 4 exponent bits with bias 7, 3 mantissa bits,
   subnormals, largest finite 448, no infinities, S.1111.111 = NaN);
-  scale = amax / 448; code = x / scale rounded to nearest-even E4M3, saturated to +-448.
+  stored scale amax / 448; code = x * (448 / amax) rounded to nearest-even E4M3,
+  saturated to +-448.
+* The page fixes no rounding order; the value coded is x times the reciprocal scale,
+  taken once per row (one division per row rather than per value).
 * A row of zeros gets scale 0 and all-zero codes.
 * Decoding: value = code * scale, rounded to bf16 (nearest-even).
 * Every quantity that decides a code is float32, computed with IEEE-rounded float32
@@ -52,18 +55,20 @@ def _row_scale(x32: np.ndarray, qmax: np.float32) -> np.ndarray:
     return (amax / qmax).astype(np.float32)
 
 
-def _scaled(x32: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """x / scale per row in float32; rows with scale 0 (all zeros) give 0."""
-    safe = np.where(scale == 0, np.float32(1), scale).astype(np.float32)
-    v = (x32 / safe[..., None]).astype(np.float32)
-    return np.where((scale == 0)[..., None], np.float32(0), v)
+def _scaled(x32: np.ndarray, qmax: np.float32) -> np.ndarray:
+    """x * (qmax / amax) per row in float32; rows of zeros give 0."""
+    amax = np.max(np.abs(x32), axis=-1)
+    safe = np.where(amax == 0, np.float32(1), amax).astype(np.float32)
+    inv = (qmax / safe).astype(np.float32)
+    v = (x32 * inv[..., None]).astype(np.float32)
+    return np.where((amax == 0)[..., None], np.float32(0), v)
 
 
 def int8_quantize(x_bits: np.ndarray):
     """bf16 rows [..., d] (uint16 bit patterns) -> (int8 codes [..., d], float32 scales [...])."""
     x32 = bf16_bits_to_f32(x_bits)
     scale = _row_scale(x32, INT8_MAX)
-    v = _scaled(x32, scale)
+    v = _scaled(x32, INT8_MAX)
     codes = np.clip(np.rint(v), -127, 127).astype(np.int8)
     return codes, scale
 
@@ -112,7 +117,7 @@ def fp8_quantize(x_bits: np.ndarray):
     """bf16 rows [..., d] (uint16 bit patterns) -> (E4M3 codes uint8 [..., d], float32 scales [...])."""
     x32 = bf16_bits_to_f32(x_bits)
     scale = _row_scale(x32, E4M3_MAX)
-    v = _scaled(x32, scale)
+    v = _scaled(x32, E4M3_MAX)
     return e4m3_encode(v), scale
 
 
