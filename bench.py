@@ -42,10 +42,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="refine_1344x768")
     p.add_argument("--topk", type=int, default=None, help="override k (e.g. all blocks for a dense run)")
-    p.add_argument("--pattern", choices=["selected", "window", "cube"], default="selected",
+    p.add_argument("--pattern", choices=["selected", "window", "cube", "quant"], default="selected",
                    help="selected: pool -> select -> fwd (the method); window: fwd alone with the static "
                         "window pattern of sol_attn_window_blocks (same k); cube: the method with 3-D "
-                        "cube blocks (tokens reordered to cube-major order, the path, outputs reordered back)")
+                        "cube blocks (tokens reordered to cube-major order, the path, outputs reordered back); "
+                        "quant: the method between the 8-bit exchange formats (Q/K/V INT8 in, output FP8 out), "
+                        "with the error against the bf16 path")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="after timing, run one plain device copy of Q (size known) to calibrate traffic counters")
@@ -68,6 +70,8 @@ def cpu_baseline(wl, q, k, v, topk, n_heads, pattern="selected"):
     ks = k.reshape(-1, wl.L, wl.d)[:n_heads]
     vs = v.reshape(-1, wl.L, wl.d)[:n_heads]
     t0 = time.perf_counter()
+    if pattern == "quant":
+        pattern = "selected"
     if pattern == "cube":
         oracle.run_cube(qs, ks, vs, wl.dtype, wl.grid, wl.cube, topk)
         what = (f"whole path with {'x'.join(map(str, wl.cube))} cube blocks (pool, scores, top-{topk}, float64 "
@@ -125,6 +129,7 @@ def main():
 
     window = args.pattern == "window"
     cube = args.pattern == "cube"
+    quant = args.pattern == "quant"
     if window:
         idx.copy_(S.sol_attn_window_blocks(nb, topk).view(1, 1, nb, topk).expand(wl.B, wl.H, nb, topk))
     T, h, w = wl.grid
@@ -136,9 +141,25 @@ def main():
         Qc, Kc, Vc, Oc = (torch.empty_like(Q) for _ in range(4))
         ny, nx = h // by, w // bx
         order = S.sol_attn_frame_order(wl.L, wl.block, wl.block * ny * nx, wl.block * nx).cuda()
+    elif quant:
+        # one GPU's share of the 8-bit exchange around the attention: Q/K/V as INT8 codes
+        # (as received), decoded, the method, the output coded as FP8 (as sent back), decoded
+        if wl.dtype != "bf16":
+            raise SystemExit("the 8-bit exchange formats take bf16 tensors")
+        Qc, Kc, Vc, Oc = (torch.empty_like(Q) for _ in range(4))
+        codes = [torch.empty(Q.shape, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        scales = [torch.empty(Q.shape[:3], dtype=torch.float32, device="cuda") for _ in range(4)]
     else:
         Qc, Kc, Vc, Oc = Q, K, V, out
     row_bytes = wl.d * Q.element_size()
+
+    def quantize(x, n, fmt):
+        S._check("quantize", lib.sol_attn_quantize(x.data_ptr(), wl.B, wl.H, wl.L, wl.d, fmt, codes[n].data_ptr(),
+                                                   scales[n].data_ptr(), s_ptr))
+
+    def dequantize(n, fmt, dst):
+        S._check("dequantize", lib.sol_attn_dequantize(codes[n].data_ptr(), scales[n].data_ptr(), wl.B, wl.H, wl.L,
+                                                       wl.d, fmt, dst.data_ptr(), s_ptr))
 
     def permute(src, dst, inverse):
         S._check("cube_permute", lib.sol_attn_cube_permute(src.data_ptr(), dst.data_ptr(), wl.B, wl.H, T, h, w,
@@ -167,6 +188,12 @@ def main():
     elif cube:
         phases = [("permute_in", run_permute_in), ("pool", run_pool), ("select", run_select), ("fwd", run_fwd),
                   ("permute_out", lambda: permute(Oc, out, True))]
+    elif quant:
+        phases = [("quant_qkv_int8", lambda: [quantize(x, n, S.INT8) for n, x in enumerate((Q, K, V))]),
+                  ("dequant_qkv", lambda: [dequantize(n, S.INT8, x) for n, x in enumerate((Qc, Kc, Vc))]),
+                  ("pool", run_pool), ("select", run_select), ("fwd", run_fwd),
+                  ("quant_o_fp8", lambda: quantize(Oc, 3, S.FP8_E4M3)),
+                  ("dequant_o", lambda: dequantize(3, S.FP8_E4M3, out))]
     else:
         phases = [("pool", run_pool), ("select", run_select), ("fwd", run_fwd)]
 
@@ -177,6 +204,39 @@ def main():
             fn()
         if ev is not None:
             ev[len(phases)].record(stream)
+
+    quant_err = None
+    if quant:
+        # error of the 8-bit exchange against the bf16 path (outside the timed region)
+        Qc, Kc, Vc, Oc, keep = Q, K, V, out, (Qc, Kc, Vc, Oc)
+        run_pool(), run_select(), run_fwd()
+        ref_out, ref_idx = out.clone(), idx.clone()
+        Qc, Kc, Vc, Oc = keep
+        step()
+        torch.cuda.synchronize()
+        diff = (out.float() - ref_out.float()).abs()
+        same = (idx.unsqueeze(-1) == ref_idx.unsqueeze(-2)).any(-1).float().mean().item()
+        changed = ~(idx == ref_idx).all(-1)                       # query blocks whose key set moved
+        row_changed = changed.repeat_interleave(wl.block, dim=-1)[..., :wl.L]
+        kept = diff[~row_changed]
+        # the FP8 round trip of the output alone (same selection, exact attention inputs)
+        quantize(ref_out, 3, S.FP8_E4M3)
+        dequantize(3, S.FP8_E4M3, Oc)
+        torch.cuda.synchronize()
+        fp8_diff = (Oc.float() - ref_out.float()).abs()
+        quant_err = {"o_max_abs_err": round(diff.max().item(), 5), "o_mean_abs_err": round(diff.mean().item(), 6),
+                     "o_rms_ref": round(ref_out.float().pow(2).mean().sqrt().item(), 5),
+                     "selected_blocks_kept": round(same, 5),
+                     "query_blocks_changed": round(changed.float().mean().item(), 5),
+                     "o_err_unchanged_blocks": {"max": round(kept.max().item(), 5),
+                                                "mean": round(kept.mean().item(), 6)},
+                     "o_err_changed_blocks": ({"max": round(diff[row_changed].max().item(), 5),
+                                               "mean": round(diff[row_changed].mean().item(), 6)}
+                                              if bool(changed.any()) else None),
+                     "o_fp8_round_trip": {"max": round(fp8_diff.max().item(), 5),
+                                          "mean": round(fp8_diff.mean().item(), 6)},
+                     "bytes_per_row": {"bf16": 2 * wl.d, "8-bit + scale": wl.d + 4}}
+        del ref_out, ref_idx, diff, kept, fp8_diff, row_changed
 
     for _ in range(args.warmup):
         step()
@@ -237,6 +297,7 @@ def main():
         **({"permute_gbs": round(4 * 2 * wl.B * wl.H * wl.L * row_bytes
                                  / ((t_phase["permute_in"] + t_phase["permute_out"]) * 1e-3) / 1e9, 1)}
            if cube else {}),
+        **({"exchange_8bit": quant_err} if quant else {}),
         "timed_wall_s": round(wall, 3),
         "input_gen_s": round(t_gen, 2),
     }

@@ -27,4 +27,10 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, int BH
 hipError_t launch_cube_permute(const void* src, void* dst, int BH, int T, int h, int w, int row_bytes, int bt,
                                int by, int bx, bool inverse, hipStream_t stream);
 
+// 8-bit exchange formats: one float32 scale per row of d bf16 values.
+hipError_t launch_quantize(const void* x, long long rows, int d, bool fp8, void* codes, float* scales,
+                           hipStream_t stream);
+hipError_t launch_dequantize(const void* codes, const float* scales, long long rows, int d, bool fp8, void* out,
+                             hipStream_t stream);
+
 }  // namespace sol_attn

@@ -152,6 +152,49 @@ int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h
                     "cube_permute launch");
 }
 
+namespace {
+
+int check_quant(const char* call, int B, int H, int L, int d, int format) {
+  if (B < 0 || H < 0 || L < 0) return fail(SOL_ATTN_ERR_SHAPE, "%s: negative size B=%d H=%d L=%d", call, B, H, L);
+  if (d <= 0) return fail(SOL_ATTN_ERR_SHAPE, "%s: d=%d must be positive", call, d);
+  if (format != SOL_ATTN_INT8 && format != SOL_ATTN_FP8_E4M3)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "%s: unknown format %d", call, format);
+  if (d % 8 != 0 || d > 512) return fail(SOL_ATTN_ERR_UNSUPPORTED, "%s needs d %% 8 == 0 and d <= 512 (d=%d)", call, d);
+  return SOL_ATTN_OK;
+}
+
+}  // namespace
+
+int sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, void* codes, float* scales,
+                      void* stream) {
+  int st = check_quant("quantize", B, H, L, d, format);
+  if (st != SOL_ATTN_OK) return st;
+  const long long rows = (long long)B * H * L;
+  if (rows == 0) return ok();
+  if (rows > 0x3fffffffLL * 16) return fail(SOL_ATTN_ERR_SHAPE, "quantize: too many rows");
+  if (!x || !codes || !scales) return fail(SOL_ATTN_ERR_NULL, "quantize: NULL pointer");
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+    return fail(SOL_ATTN_ERR_ALIGN, "quantize: x needs 16-byte, codes 8-byte, scales 4-byte alignment");
+  return hip_status(sol_attn::launch_quantize(x, rows, d, format == SOL_ATTN_FP8_E4M3, codes, scales,
+                                              static_cast<hipStream_t>(stream)),
+                    "quantize launch");
+}
+
+int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
+                        void* stream) {
+  int st = check_quant("dequantize", B, H, L, d, format);
+  if (st != SOL_ATTN_OK) return st;
+  const long long rows = (long long)B * H * L;
+  if (rows == 0) return ok();
+  if (rows > 0x3fffffffLL * 16) return fail(SOL_ATTN_ERR_SHAPE, "dequantize: too many rows");
+  if (!codes || !scales || !out) return fail(SOL_ATTN_ERR_NULL, "dequantize: NULL pointer");
+  if (!aligned(out, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+    return fail(SOL_ATTN_ERR_ALIGN, "dequantize: out needs 16-byte, codes 8-byte, scales 4-byte alignment");
+  return hip_status(sol_attn::launch_dequantize(codes, scales, rows, d, format == SOL_ATTN_FP8_E4M3, out,
+                                                static_cast<hipStream_t>(stream)),
+                    "dequantize launch");
+}
+
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
   if (block <= 0 || L < 0 || frame_tokens <= 0 || row_tokens <= 0 || row_tokens > frame_tokens)
     return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,

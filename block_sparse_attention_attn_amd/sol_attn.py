@@ -15,6 +15,8 @@ Calls (same names as the C ABI):
   sol_attn_cube_permute(x, grid, cube, inverse)      -> x with its tokens in cube-major (or frame-major) order
   sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
   cube_sparse_attention(q, k, v, grid, cube, topk)   -> the same with 3-D cube blocks
+  sol_attn_quantize(x, fmt) / sol_attn_dequantize(codes, scales, fmt)
+                                                     -> 8-bit exchange formats (INT8, FP8_E4M3)
 """
 from __future__ import annotations
 
@@ -62,6 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_window_blocks.restype = i
     lib.sol_attn_cube_permute.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, i, vp]
     lib.sol_attn_cube_permute.restype = i
+    lib.sol_attn_quantize.argtypes = [vp, i, i, i, i, i, vp, vp, vp]
+    lib.sol_attn_quantize.restype = i
+    lib.sol_attn_dequantize.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+    lib.sol_attn_dequantize.restype = i
     lib.sol_attn_last_error.argtypes = []
     lib.sol_attn_last_error.restype = ctypes.c_char_p
     lib.sol_attn_version.argtypes = []
@@ -234,6 +240,38 @@ def cube_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gri
     if return_idx:
         out.append(idx)
     return out[0] if len(out) == 1 else tuple(out)
+
+
+INT8, FP8_E4M3 = 0, 1
+
+
+def sol_attn_quantize(x: torch.Tensor, fmt: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [B,H,L,d] -> (codes uint8 [B,H,L,d] (int8 bit patterns for INT8), scales float32 [B,H,L])."""
+    lib = load_library()
+    if x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 device tensor [B,H,L,d]")
+    B, H, L, d = x.shape
+    codes = torch.empty((B, H, L, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
+    _check("sol_attn_quantize", lib.sol_attn_quantize(_ptr(x), B, H, L, d, fmt, _ptr(codes), _ptr(scales),
+                                                      _stream(x)))
+    return codes, scales
+
+
+def sol_attn_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(codes uint8 [B,H,L,d], scales float32 [B,H,L]) -> bf16 [B,H,L,d]."""
+    lib = load_library()
+    if codes.dtype not in (torch.uint8, torch.int8) or codes.dim() != 4 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous 1-byte [B,H,L,d]")
+    B, H, L, d = codes.shape
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, L) or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous float32 [B,H,L]")
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=codes.device)
+    _check("sol_attn_dequantize", lib.sol_attn_dequantize(_ptr(codes), _ptr(scales), B, H, L, d, fmt, _ptr(out),
+                                                          _stream(codes)))
+    return out
 
 
 def version() -> int:

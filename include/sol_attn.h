@@ -175,6 +175,39 @@ int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
 int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
                           int by, int bx, int inverse, void* stream);
 
+/*
+ * 8-bit exchange formats.  Between GPUs the Sol-H3 runtime sends Q, K and V as INT8 and
+ * the attention output as FP8, shrinking the exchanged data ("Videomodel MiniMax-H3
+ * rendert sneller dan afspelen", section "Waar de snelheidswinst vandaan komt": by
+ * 51.6 percent).  Each token row of one head (d values) gets one float32 scale, so a
+ * row costs d + 4 bytes instead of 2d (51.6 % of the bf16 bytes at d = 128).  With
+ * amax = max |x| over the row:
+ *   SOL_ATTN_INT8      scale = amax/127, code = round-half-even(x * (127/amax)), in [-127, 127]
+ *   SOL_ATTN_FP8_E4M3  scale = amax/448, code = x * (448/amax) rounded to nearest-even OCP
+ *                      E4M3 (bias 7, 3 mantissa bits, largest finite 448), saturated
+ * A row of zeros has scale 0 and zero codes.  Every step is float32 with IEEE rounding,
+ * so codes are reproducible bit for bit.  Decoding: code * scale, rounded to bf16.
+ */
+typedef enum { SOL_ATTN_INT8 = 0, SOL_ATTN_FP8_E4M3 = 1 } sol_attn_qformat_t;
+
+/*
+ * Quantise bf16 rows.
+ *   x       [B,H,L,d] bf16 (rows of d values); 16-byte aligned.
+ *   codes   [B,H,L,d] one byte per value (int8 or E4M3) output; 8-byte aligned.
+ *   scales  [B,H,L] float32 output (one per row); 4-byte aligned.
+ * Supported: d % 8 == 0, d <= 512.  Inputs must be finite.
+ */
+int sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, void* codes, float* scales,
+                      void* stream);
+
+/*
+ * Decode rows written by sol_attn_quantize (same format) to bf16.
+ *   codes [B,H,L,d] bytes (8-byte aligned), scales [B,H,L] float32 (4-byte aligned),
+ *   out   [B,H,L,d] bf16 output (16-byte aligned).  Same support as sol_attn_quantize.
+ */
+int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
+                        void* stream);
+
 /* Human-readable description of the last failure on the calling thread ("" if none). */
 const char* sol_attn_last_error(void);
 

@@ -21,7 +21,7 @@ def test_header_symbols_exported(lib):
     names = S.header_symbols()
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
                           "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks",
-                          "sol_attn_cube_permute"}
+                          "sol_attn_cube_permute", "sol_attn_quantize", "sol_attn_dequantize"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -143,3 +143,17 @@ def test_cube_permute_argument_checks(lib):
     assert _perm(lib, H=0, src=None) == 0              # nothing to do
     assert _perm(lib, T=0, h=0, w=0) == 0
     assert b"does not tile" in (_perm(lib, by=3), lib.sol_attn_last_error())[1]
+
+
+def test_quantize_argument_checks(lib):
+    q = lambda **kw: lib.sol_attn_quantize(kw.get("x", FAKE), kw.get("B", 1), kw.get("H", 1), kw.get("L", 8),
+                                           kw.get("d", 128), kw.get("fmt", 0), kw.get("codes", FAKE),
+                                           kw.get("scales", FAKE), None)
+    dq = lambda **kw: lib.sol_attn_dequantize(kw.get("codes", FAKE), kw.get("scales", FAKE), 1, 1, 8,
+                                              kw.get("d", 128), kw.get("fmt", 1), kw.get("out", FAKE), None)
+    assert q(L=-1) == 2 and q(d=0) == 2
+    assert q(fmt=2) == 4 and q(d=12) == 4 and q(d=520) == 4
+    assert q(x=None) == 1 and q(scales=None) == 1
+    assert q(x=MIS) == 5 and q(codes=FAKE + 4) == 5 and q(scales=FAKE + 2) == 5
+    assert q(B=0, x=None) == 0
+    assert dq(out=MIS) == 5 and dq(codes=None) == 1 and dq(d=7) == 4

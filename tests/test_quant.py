@@ -123,3 +123,111 @@ def test_fp8_zero_row_and_unit_scale():
 def test_size_ratio_is_51_6_percent_at_d128():
     d = 128
     assert abs((d + 4) / (2 * d) - 0.516) < 5e-4
+
+
+# ----------------------------------------------------------------------------- GPU parity
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_attention_attn_amd import sol_attn
+    sol_attn.load_library()
+    return sol_attn
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _every_bf16_up_to(limit, d):
+    """Rows [n, d] holding every bf16 value in [-limit, limit] (both zeros included), each
+    row also holding +limit so that its scale makes x * (qmax / amax) == x exactly."""
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = Qo.bf16_bits_to_f32(allbits)
+    keep = allbits[np.isfinite(vals) & (np.abs(vals) <= limit)]
+    per = d - 1
+    n = -(-keep.size // per)
+    body = np.resize(keep, n * per).reshape(n, per)
+    lim = Qo.bf16_bits_round(np.float32([limit]))[0]
+    return np.concatenate([np.full((n, 1), lim, np.uint16), body], axis=1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_codes_exhaustive_over_bf16_values(fmt):
+    """Unit scale (row maximum 127 or 448): every bf16 value in range is coded exactly as
+    the oracle codes it -- ties, subnormal E4M3 steps, signed zeros."""
+    S = _gpu()
+    limit = 127.0 if fmt == 0 else 448.0
+    rows = _every_bf16_up_to(limit, 128)
+    x = rows.reshape(1, 1, *rows.shape)
+    codes, scales = S.sol_attn_quantize(_dev_bf16(x), fmt)
+    torch.cuda.synchronize()
+    want_codes, want_scales = (Qo.int8_quantize if fmt == 0 else Qo.fp8_quantize)(x)
+    assert np.all(want_scales == 1.0)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint8), want_codes.view(np.uint8))
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d", [8, 64, 128, 136, 512])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_dequantize_match_oracle(fmt, d):
+    S = _gpu()
+    rng = np.random.default_rng(d + fmt)
+    B, H, L = 2, 3, 37                                  # 222 rows: a ragged last workgroup
+    x = rng.standard_normal((B, H, L, d)) * rng.uniform(1e-3, 50, (B, H, L, 1))
+    x[0, 0, 3] = 0.0                                    # a row of zeros
+    x[1, 2, 5, : d // 2] = -0.0
+    x[1, 2, 5, d // 2:] = 0.0                           # a row of signed zeros
+    x[0, 1, 7, 0] = -0.0                                # a negative zero in an ordinary row
+    bits = Qo.bf16_bits_round(x.astype(np.float32))
+    codes, scales = S.sol_attn_quantize(_dev_bf16(bits), fmt)
+    torch.cuda.synchronize()
+    q, dq = (Qo.int8_quantize, Qo.int8_dequantize) if fmt == 0 else (Qo.fp8_quantize, Qo.fp8_dequantize)
+    want_codes, want_scales = q(bits)
+    got_codes = codes.cpu().numpy()
+    assert np.array_equal(got_codes.view(np.uint8), want_codes.view(np.uint8))
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+    out = S.sol_attn_dequantize(codes, scales, fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16),
+                          dq(want_codes, want_scales))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_dequantize_every_code(fmt):
+    """Every code byte (E4M3 without its two NaN codes) decodes as the oracle decodes it."""
+    S = _gpu()
+    codes = np.array([c for c in range(256) if fmt == 0 or (c & 0x7F) != 0x7F], np.uint8)
+    codes = np.resize(codes, 8 * 256).reshape(1, 1, 8, 256)
+    scales = np.float32([[[1.0, 0.5, 3.0, 1e-3, 7.25, 0.0, 2.0 ** -20, 1234.5]]])
+    out = S.sol_attn_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), fmt)
+    torch.cuda.synchronize()
+    c = codes.view(np.int8) if fmt == 0 else codes
+    want = (Qo.int8_dequantize if fmt == 0 else Qo.fp8_dequantize)(c, scales)
+    assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), want)
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_quantize_full_size_sampled_rows():
+    """1344x768 workload Q (40 heads x 64,512 tokens): INT8 and FP8 codes and scales of
+    sampled rows equal the oracle's, and decoding matches on those rows."""
+    from block_sparse_attention_attn_amd import workloads as W
+    S = _gpu()
+    wl = W.get("refine_1344x768")
+    q, _, _ = W.make_qkv(wl)
+    X = _dev_bf16(q)
+    rows = np.random.default_rng(11).choice(wl.B * wl.H * wl.L, 4096, replace=False)
+    flat = q.reshape(-1, wl.d)[rows]
+    for fmt, (qf, dqf) in enumerate(((Qo.int8_quantize, Qo.int8_dequantize), (Qo.fp8_quantize, Qo.fp8_dequantize))):
+        codes, scales = S.sol_attn_quantize(X, fmt)
+        out = S.sol_attn_dequantize(codes, scales, fmt)
+        torch.cuda.synchronize()
+        wc, ws = qf(flat)
+        idx = torch.from_numpy(rows)
+        assert np.array_equal(codes.view(-1, wl.d)[idx.cuda()].cpu().numpy().view(np.uint8), wc.view(np.uint8))
+        assert np.array_equal(scales.view(-1)[idx.cuda()].cpu().numpy(), ws)
+        assert np.array_equal(out.view(-1, wl.d)[idx.cuda()].cpu().view(torch.int16).numpy().view(np.uint16),
+                              dqf(wc, ws))
