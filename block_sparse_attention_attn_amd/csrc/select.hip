@@ -204,7 +204,13 @@ constexpr int kMaxMfmaBlocks = 1280;   // 16 rows of keys fill 160 KiB of LDS
 constexpr int kMaxS = 32;          // d <= 128
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-template <int MAXPL>
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// kS = d / 4 when that is 16 or 32 (d = 64, 128): every contraction index exists, so a
+// lane's S doubles of Qbar and Kbar are read with unconditional 16-byte loads (rows
+// clamped into range) and the next key tile is prefetched while the current one runs
+// through the matrix cores.  kS = 0: any d <= 128, element-wise guarded loads.
+template <int MAXPL, int kS>
 __global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __restrict__ q_pooled,
                                                                const double* __restrict__ k_pooled,
                                                                int n_blocks, int d, int topk,
@@ -219,30 +225,15 @@ __global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __r
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int S = (d + 3) / 4;
+  const int S = kS > 0 ? kS : (d + 3) / 4;
   const int col = lane & 15, kk = lane >> 4;
   const int e0 = kk * S;
-
-  // A operand: Qbar[i0 + col][e0 + s]
-  double a[kMaxS];
-  {
-    const int row = min(i0 + col, n_blocks - 1);
-    const double* qr = q_pooled + ((size_t)bh * n_blocks + row) * d + e0;
-#pragma unroll
-    for (int s = 0; s < kMaxS; ++s) a[s] = (s < S && e0 + s < d && col < nrows) ? qr[s] : 0.0;
-  }
   const double* kbase = k_pooled + (size_t)bh * n_blocks * d;
-  for (int j0 = wave * 16; j0 < n_blocks; j0 += kWaves * 16) {
+  const double* qr = q_pooled + ((size_t)bh * n_blocks + min(i0 + col, n_blocks - 1)) * d + e0;
+
+  // scores r_ij of one 16x16 tile (key blocks j0 .. j0+15) into the LDS key rows
+  auto store_tile = [&](const f64x4& c, int j0) {
     const int j = j0 + col;
-    const double* kr = kbase + (size_t)min(j, n_blocks - 1) * d + e0;
-    f64x4 c = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {
-      if (s < S) {
-        const double b = (e0 + s < d && j < n_blocks) ? kr[s] : 0.0;
-        c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b, c, 0, 0, 0);
-      }
-    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * r + kk;
@@ -251,9 +242,74 @@ __global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __r
         if (scores) scores[((size_t)bh * n_blocks + i0 + i) * n_blocks + j] = c[r] / sqrt_d;
       }
     }
+  };
+
+  if constexpr (kS > 0) {
+    constexpr int kV = kS / 2;                       // 16-byte vectors per lane and row
+    f64x2 a[kV], b[kV], nb[kV];
+#pragma unroll
+    for (int t = 0; t < kV; ++t) {
+      const f64x2 x = *reinterpret_cast<const f64x2*>(qr + 2 * t);
+      a[t] = col < nrows ? x : f64x2{0.0, 0.0};
+    }
+    auto load_keys = [&](int j0, f64x2 (&dst)[kV]) {
+      const double* kr = kbase + (size_t)min(j0 + col, n_blocks - 1) * d + e0;
+#pragma unroll
+      for (int t = 0; t < kV; ++t) dst[t] = *reinterpret_cast<const f64x2*>(kr + 2 * t);
+    };
+    int j0 = wave * 16;
+    if (j0 < n_blocks) load_keys(j0, nb);
+    for (; j0 < n_blocks; j0 += kWaves * 16) {
+#pragma unroll
+      for (int t = 0; t < kV; ++t) b[t] = nb[t];
+      if (j0 + kWaves * 16 < n_blocks) load_keys(j0 + kWaves * 16, nb);
+      f64x4 c = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s = 0; s < kS; ++s) c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s / 2][s % 2], b[s / 2][s % 2], c, 0, 0, 0);
+      store_tile(c, j0);
+    }
+  } else {
+    double a[kMaxS];
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) a[s] = (s < S && e0 + s < d && col < nrows) ? qr[s] : 0.0;
+    for (int j0 = wave * 16; j0 < n_blocks; j0 += kWaves * 16) {
+      const int j = j0 + col;
+      const double* kr = kbase + (size_t)min(j, n_blocks - 1) * d + e0;
+      f64x4 c = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s = 0; s < kMaxS; ++s) {
+        if (s < S) {
+          const double bv = (e0 + s < d && j < n_blocks) ? kr[s] : 0.0;
+          c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], bv, c, 0, 0, 0);
+        }
+      }
+      store_tile(c, j0);
+    }
   }
   __syncthreads();
   topk_rows_reg<MAXPL>(keys, n_blocks, topk, nrows, wave, lane, block_idx + ((size_t)bh * n_blocks + i0) * topk);
+}
+
+template <int kS>
+hipError_t launch_select_mfma(const double* q_pooled, const double* k_pooled, int BH, int n_blocks, int d,
+                              int topk, int32_t* block_idx, double* scores_or_null, hipStream_t stream) {
+  const size_t lds = (size_t)kMfmaRows * n_blocks * 8;
+  const int per_lane = (n_blocks + 63) / 64;
+  // keys cached per lane in the top-k phase: the smallest instantiation that holds them
+  auto kern = per_lane <= 4 ? select_mfma_kernel<4, kS>
+            : per_lane <= 8 ? select_mfma_kernel<8, kS>
+            : per_lane <= 16 ? select_mfma_kernel<16, kS>
+            : select_mfma_kernel<(kMaxMfmaBlocks + 63) / 64, kS>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return err;
+  }
+  dim3 grid((n_blocks + kMfmaRows - 1) / kMfmaRows, BH);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, q_pooled, k_pooled, n_blocks, d, topk, block_idx,
+                     scores_or_null, sqrt((double)d));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -263,23 +319,11 @@ hipError_t launch_select(const double* q_pooled, const double* k_pooled, int BH,
   (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
   const size_t budget = 160 * 1024;
   if (d <= 4 * kMaxS && n_blocks <= kMaxMfmaBlocks) {
-    const size_t lds = (size_t)kMfmaRows * n_blocks * 8;
-    const int per_lane = (n_blocks + 63) / 64;
-    // keys cached per lane in the top-k phase: the smallest instantiation that holds them
-    auto kern = per_lane <= 4 ? select_mfma_kernel<4>
-              : per_lane <= 8 ? select_mfma_kernel<8>
-              : per_lane <= 16 ? select_mfma_kernel<16>
-              : select_mfma_kernel<(kMaxMfmaBlocks + 63) / 64>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) {
-      (void)hipGetLastError();
-      return err;
-    }
-    dim3 grid((n_blocks + kMfmaRows - 1) / kMfmaRows, BH);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, q_pooled, k_pooled, n_blocks, d, topk, block_idx,
-                       scores_or_null, sqrt((double)d));
-    return hipGetLastError();
+    if (d == 128)
+      return launch_select_mfma<32>(q_pooled, k_pooled, BH, n_blocks, d, topk, block_idx, scores_or_null, stream);
+    if (d == 64)
+      return launch_select_mfma<16>(q_pooled, k_pooled, BH, n_blocks, d, topk, block_idx, scores_or_null, stream);
+    return launch_select_mfma<0>(q_pooled, k_pooled, BH, n_blocks, d, topk, block_idx, scores_or_null, stream);
   }
   // general path: rows per workgroup as many as fit (<= 8) in 160 KiB of LDS
   int rows = kMaxRows;
