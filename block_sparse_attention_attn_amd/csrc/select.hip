@@ -18,9 +18,13 @@
 //      owns key block j = chunk + l and forms the dot products of its rows
 //      (float64 FMA; wave w takes rows w, w+4, ...), storing an order-preserving
 //      64-bit key of r_ij in LDS (and optionally r_ij / sqrt(d)).
-//   3. One wave per row finds the k-th largest key T by a 64-step bitwise
-//      search: a candidate threshold is accepted if at least topk keys are >= it;
-//      counts come from wave ballots + popcount.  Lane l owns keys j = 64*t + l.
+//   3. One wave per row finds a threshold T by a bitwise search from the top bit:
+//      a candidate threshold is accepted if at least topk keys are >= it; counts
+//      come from wave ballots + popcount.  Lane l owns keys j = 64*t + l.  The
+//      search stops as soon as exactly topk keys are >= the candidate (those keys
+//      are then the top k, with no tie at the boundary), which for real score gaps
+//      happens after ~20-30 of the 64 bits; only an exact tie at the k-th place
+//      runs all 64 steps, ending at the k-th largest key itself.
 //   4. Keys > T are taken, plus the first (topk - #(>T)) keys == T in ascending
 //      j.  With interleaved ownership, ascending j is (t, lane) order, so a key's
 //      output position is a running count plus the popcount of the ballot bits
@@ -55,7 +59,9 @@ __device__ __forceinline__ void topk_rows(const uint64_t* keys, int n_blocks, in
   const int per_lane = (n_blocks + 63) / 64;
   for (int r = wave; r < nrows; r += kWaves) {
     const uint64_t* rk = keys + (size_t)r * n_blocks;
-    // k-th largest key value: the largest T with #(key >= T) >= topk (keys are >= 1)
+    // threshold T with #(key >= T) >= topk whose keys > T plus the first keys == T in
+    // ascending j are the top k: either #(key >= T) == topk, or T is the k-th largest
+    // key (keys are >= 1)
     uint64_t T = 0;
     for (int bit = 63; bit >= 0; --bit) {
       const uint64_t cand = T | (1ull << bit);
@@ -66,13 +72,14 @@ __device__ __forceinline__ void topk_rows(const uint64_t* keys, int n_blocks, in
         cnt += __popcll(__ballot(ge));
       }
       if (cnt >= topk) T = cand;
+      if (cnt == topk) break;       // keys >= T are exactly the top k
     }
     int tot_gt = 0;
     for (int t = 0; t < per_lane; ++t) {
       const int j = 64 * t + lane;
       tot_gt += __popcll(__ballot(j < n_blocks && rk[min(j, n_blocks - 1)] > T));
     }
-    const int need_eq = topk - tot_gt;     // >= 1 by the choice of T
+    const int need_eq = topk - tot_gt;     // keys == T still to take (0 if T is no key)
     int32_t* out = out_rows + (size_t)r * topk;
     int base = 0, eq_seen = 0;
     const uint64_t below = lanes_below(lane);
@@ -111,6 +118,7 @@ __device__ __forceinline__ void topk_rows_reg(const uint64_t* keys, int n_blocks
 #pragma unroll
       for (int t = 0; t < MAXPL; ++t) cnt += __popcll(__ballot(x[t] >= cand));
       if (cnt >= topk) T = cand;
+      if (cnt == topk) break;       // keys >= T are exactly the top k
     }
     int tot_gt = 0;
 #pragma unroll
