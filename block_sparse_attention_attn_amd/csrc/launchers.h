@@ -33,4 +33,8 @@ hipError_t launch_quantize(const void* x, long long rows, int d, bool fp8, void*
 hipError_t launch_dequantize(const void* codes, const float* scales, long long rows, int d, bool fp8, void* out,
                              hipStream_t stream);
 
+// Count of block-index rows with an entry out of range or not strictly ascending.
+hipError_t launch_check_block_idx(const int32_t* idx, long long rows, int n_blocks, int topk, int32_t* bad_rows,
+                                  hipStream_t stream);
+
 }  // namespace sol_attn

@@ -195,6 +195,22 @@ int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, in
                     "dequantize launch");
 }
 
+int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_blocks, int topk, int32_t* bad_rows,
+                             void* stream) {
+  if (B < 0 || H < 0 || n_blocks < 0 || topk < 0)
+    return fail(SOL_ATTN_ERR_SHAPE, "check_block_idx: negative size B=%d H=%d n_blocks=%d topk=%d", B, H, n_blocks,
+                topk);
+  if (!bad_rows) return fail(SOL_ATTN_ERR_NULL, "check_block_idx: NULL bad_rows");
+  const long long rows = (long long)B * H * n_blocks;
+  if (rows > 0 && topk > 0 && !block_idx) return fail(SOL_ATTN_ERR_NULL, "check_block_idx: NULL block_idx");
+  if (!aligned(bad_rows, 4) || (block_idx && !aligned(block_idx, 4)))
+    return fail(SOL_ATTN_ERR_ALIGN, "check_block_idx: pointers not 4-byte aligned");
+  if (rows / 4 > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "check_block_idx: too many rows");
+  return hip_status(sol_attn::launch_check_block_idx(block_idx, topk > 0 ? rows : 0, n_blocks, topk, bad_rows,
+                                                     static_cast<hipStream_t>(stream)),
+                    "check_block_idx launch");
+}
+
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
   if (block <= 0 || L < 0 || frame_tokens <= 0 || row_tokens <= 0 || row_tokens > frame_tokens)
     return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,

@@ -12,6 +12,7 @@ Calls (same names as the C ABI):
   sol_attn_fwd(q, k, v, block_idx, block, ...)       -> out [B,H,L,d] (+ lse float32 [B,H,L])
   sol_attn_frame_order(L, block, frame_tokens, row_tokens) -> int32 schedule of the query blocks
   sol_attn_window_blocks(n_blocks, topk)             -> int32 [n_blocks, topk] static window pattern
+  sol_attn_check_block_idx(block_idx)                -> rows of an index list sol_attn_fwd does not accept
   sol_attn_cube_permute(x, grid, cube, inverse)      -> x with its tokens in cube-major (or frame-major) order
   sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
   cube_sparse_attention(q, k, v, grid, cube, topk)   -> the same with 3-D cube blocks
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_quantize.restype = i
     lib.sol_attn_dequantize.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
     lib.sol_attn_dequantize.restype = i
+    lib.sol_attn_check_block_idx.argtypes = [vp, i, i, i, i, vp, vp]
+    lib.sol_attn_check_block_idx.restype = i
     lib.sol_attn_last_error.argtypes = []
     lib.sol_attn_last_error.restype = ctypes.c_char_p
     lib.sol_attn_version.argtypes = []
@@ -141,6 +144,20 @@ def sol_attn_select(q_pooled: torch.Tensor, k_pooled: torch.Tensor, topk: int, r
     _check("sol_attn_select", lib.sol_attn_select(_ptr(q_pooled), _ptr(k_pooled), B, H, nb, d, topk, _ptr(idx),
                                                   _ptr(scores), _stream(q_pooled)))
     return (idx, scores) if return_scores else idx
+
+
+def sol_attn_check_block_idx(block_idx: torch.Tensor, n_blocks: Optional[int] = None) -> int:
+    """Number of rows of an int32 [B,H,nB,topk] device list that sol_attn_fwd does not accept
+    (an entry outside [0, nB) or not strictly ascending); synchronises the stream."""
+    lib = load_library()
+    if block_idx.dtype != torch.int32 or block_idx.dim() != 4 or not block_idx.is_contiguous() or not block_idx.is_cuda:
+        raise ValueError("block_idx must be a contiguous int32 device tensor [B,H,nB,topk]")
+    B, H, nb, topk = block_idx.shape
+    bad = torch.empty(1, dtype=torch.int32, device=block_idx.device)
+    _check("sol_attn_check_block_idx", lib.sol_attn_check_block_idx(_ptr(block_idx), B, H, nb if n_blocks is None
+                                                                    else n_blocks, topk, _ptr(bad),
+                                                                    _stream(block_idx)))
+    return int(bad.item())
 
 
 def sol_attn_frame_order(L: int, block: int, frame_tokens: int, row_tokens: int) -> torch.Tensor:

@@ -100,9 +100,11 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
  * Block-sparse exact softmax attention over the selected key blocks.
  *   q, k, v        [B,H,L,d] of `dtype`; 16-byte aligned.
  *   block_idx      int32 [B,H,n_blocks,topk]; every entry must lie in [0, n_blocks) and the
- *                  entries of a row must be distinct (sol_attn_select guarantees both).
- *                  Out-of-range entries are clamped into range instead of faulting; the
- *                  affected rows' results are then unspecified.
+ *                  entries of a row must be strictly ascending (sol_attn_select and
+ *                  sol_attn_window_blocks emit such rows; sol_attn_check_block_idx checks a
+ *                  list on the device).  Out-of-range entries are clamped into range
+ *                  instead of faulting, and other orders never fault either; the affected
+ *                  rows' results are then unspecified.
  *   qblock_order_or_null
  *                  optional int32 [n_blocks] device array: a permutation of the query blocks
  *                  giving the order in which they are scheduled (shared by all (b,h)).
@@ -121,6 +123,20 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
 int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
                  int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
                  float softmax_scale, void* out, float* lse_or_null, void* stream);
+
+/*
+ * Device-side validation of a block index list (for lists not made by sol_attn_select,
+ * e.g. static patterns): counts the rows of block_idx [B,H,n_blocks,topk] that
+ * sol_attn_fwd does not accept -- an entry outside [0, n_blocks), or entries that are
+ * not strictly ascending (a repeated entry included).
+ *   bad_rows  device int32 output: the number of such rows (0: the list is valid).  It
+ *             is zeroed and then counted on `stream`; read it after synchronising.
+ * Returns SOL_ATTN_ERR_SHAPE for negative sizes, SOL_ATTN_ERR_NULL for a NULL bad_rows
+ * (or a NULL block_idx with rows to check), SOL_ATTN_ERR_ALIGN for pointers not 4-byte
+ * aligned.  topk == 0 or no rows: bad_rows is set to 0.
+ */
+int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_blocks, int topk, int32_t* bad_rows,
+                             void* stream);
 
 /*
  * Host helper (no GPU work): a query-block schedule for frame-major video tokens.

@@ -21,7 +21,8 @@ def test_header_symbols_exported(lib):
     names = S.header_symbols()
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
                           "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks",
-                          "sol_attn_cube_permute", "sol_attn_quantize", "sol_attn_dequantize"}
+                          "sol_attn_cube_permute", "sol_attn_quantize", "sol_attn_dequantize",
+                          "sol_attn_check_block_idx"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -157,3 +158,10 @@ def test_quantize_argument_checks(lib):
     assert q(x=MIS) == 5 and q(codes=FAKE + 4) == 5 and q(scales=FAKE + 2) == 5
     assert q(B=0, x=None) == 0
     assert dq(out=MIS) == 5 and dq(codes=None) == 1 and dq(d=7) == 4
+
+
+def test_check_block_idx_argument_checks(lib):
+    chk = lambda idx=FAKE, B=1, H=1, nb=8, k=2, bad=FAKE: lib.sol_attn_check_block_idx(idx, B, H, nb, k, bad, None)
+    assert chk(B=-1) == 2 and chk(k=-1) == 2
+    assert chk(bad=None) == 1 and chk(idx=None) == 1
+    assert chk(bad=FAKE + 2) == 5 and chk(idx=FAKE + 1) == 5
