@@ -67,7 +67,6 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units: probabilities stay <= 256
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-constexpr int kSchedValu = 0x002;
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
