@@ -258,8 +258,15 @@ def main():
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    t_phase = {name: float(np.mean([e[n].elapsed_time(e[n + 1]) for e in evs])) for n, (name, _) in enumerate(phases)}
-    t_pool, t_fwd = t_phase.get("pool"), t_phase["fwd"]
+    samples = {name: np.array([e[n].elapsed_time(e[n + 1]) for e in evs]) for n, (name, _) in enumerate(phases)}
+    t_phase = {name: float(np.mean(x)) for name, x in samples.items()}
+    t_pool, t_sel, t_fwd = t_phase.get("pool"), t_phase.get("select"), t_phase["fwd"]
+    fwd_stats = {"mean": round(t_fwd, 4), "median": round(float(np.median(samples["fwd"])), 4),
+                 "min": round(float(np.min(samples["fwd"])), 4),
+                 "p90": round(float(np.percentile(samples["fwd"], 90)), 4)}
+
+    # the matrix rate the chip sustains (diagnostic kernel, outside the timed region)
+    mfma_tflops = S.sol_attn_probe_mfma()
 
     if args.copy_probe:
         out.copy_(Q)
@@ -289,7 +296,15 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {name: round(t, 4) for name, t in t_phase.items()},
         "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_ms_stats": fwd_stats,
+        "mfma_measured_tflops": round(mfma_tflops, 1),
+        "fwd_pct_measured_mfma": round(100.0 * fwd_tflops / mfma_tflops, 2),
         "pool_gbs": None if t_pool is None else round(pool_bytes / (t_pool * 1e-3) / 1e9, 1),
+        # select: pooled float64 in + int32 indices out; 2*nB^2*d float64 flops per head
+        "select_gbs": None if t_sel is None else round(
+            (2 * wl.B * wl.H * nb * wl.d * 8 + wl.B * wl.H * nb * topk * 4) / (t_sel * 1e-3) / 1e9, 1),
+        "select_fp64_gflops": None if t_sel is None else round(
+            2.0 * wl.B * wl.H * nb * nb * wl.d / (t_sel * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": FWD_TRAFFIC_BYTES if (wl.name == "refine_1344x768" and topk == wl.topk

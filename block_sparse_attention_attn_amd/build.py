@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsol_attn.so")
-SOURCES = ["sol_attn_api.cpp", "pool.hip", "select.hip", "fwd_bf16.hip", "fwd_f32.hip", "cube.hip", "quant.hip", "check.hip"]
+SOURCES = ["sol_attn_api.cpp", "pool.hip", "select.hip", "fwd_bf16.hip", "fwd_f32.hip", "cube.hip", "quant.hip", "check.hip", "probe_mfma.hip"]
 
 
 def hipcc() -> str:

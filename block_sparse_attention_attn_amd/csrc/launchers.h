@@ -37,4 +37,7 @@ hipError_t launch_dequantize(const void* codes, const float* scales, long long r
 hipError_t launch_check_block_idx(const int32_t* idx, long long rows, int n_blocks, int topk, int32_t* bad_rows,
                                   hipStream_t stream);
 
+// Diagnostic matrix-core rate kernel (independent bf16 32x32x16 product chains).
+hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t stream);
+
 }  // namespace sol_attn

@@ -211,6 +211,14 @@ int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_block
                     "check_block_idx launch");
 }
 
+int sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream) {
+  if (workgroups < 1 || iters < 1) return fail(SOL_ATTN_ERR_SHAPE, "probe_mfma: workgroups and iters must be >= 1");
+  if (!sink) return fail(SOL_ATTN_ERR_NULL, "probe_mfma: NULL sink");
+  if (!aligned(sink, 4)) return fail(SOL_ATTN_ERR_ALIGN, "probe_mfma: sink not 4-byte aligned");
+  return hip_status(sol_attn::launch_probe_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream)),
+                    "probe_mfma launch");
+}
+
 int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
   if (block <= 0 || L < 0 || frame_tokens <= 0 || row_tokens <= 0 || row_tokens > frame_tokens)
     return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,

@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_dequantize.restype = i
     lib.sol_attn_check_block_idx.argtypes = [vp, i, i, i, i, vp, vp]
     lib.sol_attn_check_block_idx.restype = i
+    lib.sol_attn_probe_mfma.argtypes = [i, i, vp, vp]
+    lib.sol_attn_probe_mfma.restype = i
     lib.sol_attn_last_error.argtypes = []
     lib.sol_attn_last_error.restype = ctypes.c_char_p
     lib.sol_attn_version.argtypes = []
@@ -289,6 +291,27 @@ def sol_attn_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int,
     _check("sol_attn_dequantize", lib.sol_attn_dequantize(_ptr(codes), _ptr(scales), B, H, L, d, fmt, _ptr(out),
                                                           _stream(codes)))
     return out
+
+
+def sol_attn_probe_mfma(workgroups: int = 1024, iters: int = 20000, repeats: int = 5) -> float:
+    """Sustained bf16 matrix-core rate (TFLOP/s) of the current device, from timing the
+    diagnostic kernel (best of `repeats` launches after one warm-up)."""
+    lib = load_library()
+    sink = torch.empty(workgroups, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: _check("sol_attn_probe_mfma", lib.sol_attn_probe_mfma(workgroups, iters, _ptr(sink),
+                                                                         stream.cuda_stream))
+    call()
+    best = None
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return workgroups * 4 * iters * 4 * 32768.0 / (best * 1e-3) / 1e12
 
 
 def version() -> int:

@@ -224,6 +224,17 @@ int sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, voi
 int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
                         void* stream);
 
+/*
+ * Diagnostic (not part of the method): launches `workgroups` workgroups of 4 waves, each
+ * wave running `iters` x 4 independent bf16 32x32x16 matrix-core products on register
+ * operands (32768 flops each), no memory traffic.  Timing the launch gives the matrix
+ * rate the chip sustains, a practical ceiling beside the nominal 2516.6 TFLOP/s.
+ *   sink  device float[workgroups], written only in a case that does not occur (it keeps
+ *         the products from being optimised away); 4-byte aligned.
+ * Returns SOL_ATTN_ERR_SHAPE unless workgroups, iters >= 1; SOL_ATTN_ERR_NULL for a NULL sink.
+ */
+int sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream);
+
 /* Human-readable description of the last failure on the calling thread ("" if none). */
 const char* sol_attn_last_error(void);
 

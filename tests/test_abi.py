@@ -22,7 +22,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
                           "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks",
                           "sol_attn_cube_permute", "sol_attn_quantize", "sol_attn_dequantize",
-                          "sol_attn_check_block_idx"}
+                          "sol_attn_check_block_idx", "sol_attn_probe_mfma"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -165,3 +165,10 @@ def test_check_block_idx_argument_checks(lib):
     assert chk(B=-1) == 2 and chk(k=-1) == 2
     assert chk(bad=None) == 1 and chk(idx=None) == 1
     assert chk(bad=FAKE + 2) == 5 and chk(idx=FAKE + 1) == 5
+
+
+def test_probe_mfma_argument_checks(lib):
+    assert lib.sol_attn_probe_mfma(0, 10, FAKE, None) == 2
+    assert lib.sol_attn_probe_mfma(4, 0, FAKE, None) == 2
+    assert lib.sol_attn_probe_mfma(4, 10, None, None) == 1
+    assert lib.sol_attn_probe_mfma(4, 10, FAKE + 2, None) == 5
