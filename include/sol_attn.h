@@ -20,6 +20,13 @@
  *                    softmax(q k^T * scale) over the tokens of its selected key
  *                    blocks only; no mask.
  *
+ * Around them: sol_attn_cube_permute (3-D cube blocks instead of runs of tokens),
+ * sol_attn_window_blocks (a static windowed pattern for sol_attn_fwd),
+ * sol_attn_check_block_idx (device check of an index list), sol_attn_frame_order (a
+ * cache-friendly query-block schedule), sol_attn_quantize / sol_attn_dequantize (the
+ * INT8 / FP8 formats of the exchange between GPUs) and sol_attn_probe_mfma (a
+ * diagnostic of the sustained matrix-core rate).
+ *
  * Layout.  Q, K, V and O are contiguous [B, H, L, d] row-major (d fastest), in the
  * element type given by `dtype`.  Pooled tensors are [B, H, n_blocks, d] float64.
  * The block index list is int32 [B, H, n_blocks, topk], ascending per row.
@@ -36,7 +43,8 @@
  * launch returns SOL_ATTN_ERR_HIP.  sol_attn_last_error() describes the most
  * recent failure on the calling thread.  Faults inside a kernel surface at the
  * caller's next synchronisation, as for any HIP library.  Problems with zero
- * elements (B*H*L == 0) are valid and enqueue nothing.
+ * elements (B*H*L == 0) are valid and enqueue nothing (sol_attn_check_block_idx still
+ * writes its count of 0).
  */
 #ifndef SOL_ATTN_H_
 #define SOL_ATTN_H_
@@ -47,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SOL_ATTN_VERSION 100  /* major*100 + minor */
+#define SOL_ATTN_VERSION 101  /* major*100 + minor */
 
 typedef enum {
   SOL_ATTN_BF16 = 0,  /* bfloat16 inputs/outputs, float32 accumulation */

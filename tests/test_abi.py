@@ -29,7 +29,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_version(lib):
-    assert lib.sol_attn_version() == 100
+    assert lib.sol_attn_version() == 101
 
 
 FAKE = 0x10000      # 64 KiB-aligned dummy "device" address; never dereferenced
