@@ -224,6 +224,17 @@ def main():
         dequantize(3, S.FP8_E4M3, Oc)
         torch.cuda.synchronize()
         fp8_diff = (Oc.float() - ref_out.float()).abs()
+        # the same exchange with the selection made from the exact pooled means (a sender
+        # can ship float64 block sums beside the codes): only the attention sees 8-bit data
+        idx.copy_(ref_idx)
+        for n, x in enumerate((Q, K, V)):
+            quantize(x, n, S.INT8)
+            dequantize(n, S.INT8, (Qc, Kc, Vc)[n])
+        run_fwd()
+        quantize(Oc, 3, S.FP8_E4M3)
+        dequantize(3, S.FP8_E4M3, Oc)
+        torch.cuda.synchronize()
+        exact_sel_diff = (Oc.float() - ref_out.float()).abs()
         quant_err = {"o_max_abs_err": round(diff.max().item(), 5), "o_mean_abs_err": round(diff.mean().item(), 6),
                      "o_rms_ref": round(ref_out.float().pow(2).mean().sqrt().item(), 5),
                      "selected_blocks_kept": round(same, 5),
@@ -235,8 +246,10 @@ def main():
                                               if bool(changed.any()) else None),
                      "o_fp8_round_trip": {"max": round(fp8_diff.max().item(), 5),
                                           "mean": round(fp8_diff.mean().item(), 6)},
+                     "o_err_selection_from_exact_means": {"max": round(exact_sel_diff.max().item(), 5),
+                                                          "mean": round(exact_sel_diff.mean().item(), 6)},
                      "bytes_per_row": {"bf16": 2 * wl.d, "8-bit + scale": wl.d + 4}}
-        del ref_out, ref_idx, diff, kept, fp8_diff, row_changed
+        del ref_out, ref_idx, diff, kept, fp8_diff, row_changed, exact_sel_diff
 
     for _ in range(args.warmup):
         step()
