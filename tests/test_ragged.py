@@ -1,7 +1,7 @@
 """Short last block (block does not divide L) through the whole path on the GPU, against
 the float64 oracle: pooled means and selections bit-exact, outputs within the bf16 /
-fp32 tolerances, rows past L never written, and the same kernels as the aligned case
-(pair kernel for k <= 128, one block per workgroup beyond).  The oracle's reading of a
+fp32 tolerances, rows past L never written, the short block met at every position of
+the attention kernel's buffer rotation (k from 1 to all blocks).  The oracle's reading of a
 short block is pinned on the CPU in test_oracle.py."""
 import dataclasses
 import math
@@ -73,8 +73,9 @@ def _check_whole_path(S, B, H, L, d, block, topk, dtype, seed, order=None):
     assert np.abs(lse_c.double().cpu().numpy() - ref["lse"]).max() <= (1e-2 if dtype == "bf16" else 1e-5)
 
 
-@pytest.mark.parametrize("L,topk", [(1025, 3), (1087, 4), (1088, 9), (1089, 2), (1151, 9), (1151, 1), (130, 2)])
-def test_ragged_bf16_pair_kernel(S, L, topk):
+@pytest.mark.parametrize("L,topk", [(1025, 3), (1087, 4), (1088, 9), (1089, 2), (1151, 9), (1151, 1), (130, 2),
+                                    (1025, 5), (1087, 6), (1151, 7), (1089, 8)])
+def test_ragged_bf16_small_k(S, L, topk):
     """Short last block of 1, 63, 64, 65 and 127 tokens; odd and even block counts; k = all."""
     _check_whole_path(S, 1, 2, L, 128, 128, topk, "bf16", seed=L + topk)
 
@@ -91,7 +92,7 @@ def test_ragged_fp32(S, L, block, topk):
 
 
 def test_ragged_bf16_many_blocks(S):
-    """k above 128 (one query block per workgroup) with a short last block: 130 blocks,
+    """k above 128 with a short last block: 130 blocks,
     the last with 50 tokens, all of them selected (dense), checked on sampled blocks."""
     L, d, block = 129 * 128 + 50, 128, 128
     nb = 130
