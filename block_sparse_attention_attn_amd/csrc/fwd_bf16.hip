@@ -261,8 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int this_blk = cur_blk;
     const int next_blk = blk(t + 1);
     cur_blk = next_blk;
-    // all waves are done with K(t) (S_t, step t-1) and V(t-1) (PV, step t-1); this
-    // wave's copies of K(t+1) and V(t) have landed -- the barrier makes every wave's
+    // this wave's copies of K(t+1) and V(t) have landed (only its four copies of
+    // K(t+2), the youngest, may still be in flight) and its LDS reads are done; after
+    // the barrier every wave's copies are in LDS and every wave is done with K(t)
+    // (read for S_t in step t-1) and V(t-1), whose buffers this step refills
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
