@@ -132,6 +132,8 @@ def main():
     quant = args.pattern == "quant"
     if window:
         idx.copy_(S.sol_attn_window_blocks(nb, topk).view(1, 1, nb, topk).expand(wl.B, wl.H, nb, topk))
+        # a window's tiles are shared by consecutive query blocks: run them side by side
+        order = torch.arange(nb, dtype=torch.int32, device="cuda")
     T, h, w = wl.grid
     bt, by, bx = wl.cube
     if cube:
