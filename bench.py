@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are
 # what the same counters read for a plain copy of known size in the same command).
 # Set to None whenever the kernel changes until it is measured again.
-FWD_TRAFFIC_BYTES = 49523346995   # fwd_bf16_kernel, measured
+FWD_TRAFFIC_BYTES = 48939207475   # fwd_bf16_kernel<false>, measured
 
 
 def parse():
@@ -45,9 +45,12 @@ def parse():
     p.add_argument("--pattern", choices=["selected", "window", "cube", "quant"], default="selected",
                    help="selected: pool -> select -> fwd (the method); window: fwd alone with the static "
                         "window pattern of sol_attn_window_blocks (same k); cube: the method with 3-D "
-                        "cube blocks (tokens reordered to cube-major order, the path, outputs reordered back); "
+                        "cube blocks read in place from the frame-major tensors (pool_cube, select, fwd_cube); "
                         "quant: the method between the 8-bit exchange formats (Q/K/V INT8 in, output FP8 out), "
                         "with the error against the bf16 path")
+    p.add_argument("--cube-reorder", action="store_true",
+                   help="cube pattern through reordered copies instead: cube_permute Q/K/V to cube-major "
+                        "order, pool -> select -> fwd, cube_permute O back")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="after timing, run one plain device copy of Q (size known) to calibrate traffic counters")
@@ -95,7 +98,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the sparse-attention path has no "
-              f"multi-GPU mode in this build", file=sys.stderr)
+              f"multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     import torch
     from block_sparse_attention_attn_amd import sol_attn as S
@@ -136,11 +139,13 @@ def main():
         order = torch.arange(nb, dtype=torch.int32, device="cuda")
     T, h, w = wl.grid
     bt, by, bx = wl.cube
+    reorder = cube and args.cube_reorder
     if cube:
-        # boxes of bt x by x bx latents: tokens reordered to cube-major order, blocks of one box
+        # boxes of bt x by x bx latents, read in place (or, with --cube-reorder, tokens
+        # reordered to cube-major order so that a block of consecutive tokens is one box)
         if bt * by * bx != wl.block:
             raise SystemExit(f"cube {wl.cube} does not hold one block of {wl.block} tokens")
-        Qc, Kc, Vc, Oc = (torch.empty_like(Q) for _ in range(4))
+        Qc, Kc, Vc, Oc = (torch.empty_like(Q) for _ in range(4)) if reorder else (Q, K, V, out)
         ny, nx = h // by, w // bx
         order = S.sol_attn_frame_order(wl.L, wl.block, wl.block * ny * nx, wl.block * nx).cuda()
     elif quant:
@@ -180,6 +185,15 @@ def main():
                                          wl.block, topk, idx.data_ptr(), order.data_ptr(), 0.0, Oc.data_ptr(),
                                          None, s_ptr))
 
+    def run_pool_cube():
+        S._check("pool_cube", lib.sol_attn_pool_cube(Q.data_ptr(), K.data_ptr(), dtc, wl.B, wl.H, T, h, w, wl.d,
+                                                     bt, by, bx, qp.data_ptr(), kp.data_ptr(), s_ptr))
+
+    def run_fwd_cube():
+        S._check("fwd_cube", lib.sol_attn_fwd_cube(Q.data_ptr(), K.data_ptr(), V.data_ptr(), wl.B, wl.H, T, h, w,
+                                                   bt, by, bx, topk, idx.data_ptr(), order.data_ptr(), 0.0,
+                                                   out.data_ptr(), None, s_ptr))
+
     def run_permute_in():
         for src, dst in ((Q, Qc), (K, Kc), (V, Vc)):
             permute(src, dst, False)
@@ -187,9 +201,11 @@ def main():
     # the phases of one step, timed one by one in a separate pass
     if window:      # static pattern: the step is the attention alone
         phases = [("fwd", run_fwd)]
-    elif cube:
+    elif reorder:
         phases = [("permute_in", run_permute_in), ("pool", run_pool), ("select", run_select), ("fwd", run_fwd),
                   ("permute_out", lambda: permute(Oc, out, True))]
+    elif cube:
+        phases = [("pool", run_pool_cube), ("select", run_select), ("fwd", run_fwd_cube)]
     elif quant:
         phases = [("quant_qkv_int8", lambda: [quantize(x, n, S.INT8) for n, x in enumerate((Q, K, V))]),
                   ("dequant_qkv", lambda: [dequantize(n, S.INT8, x) for n, x in enumerate((Qc, Kc, Vc))]),
@@ -304,7 +320,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded smooth field + noise, unit RMS)",
-        "config": {"workload": wl.name + ("+" + args.pattern if args.pattern != "selected" else ""), "B": wl.B,
+        "config": {"workload": wl.name + ("+" + args.pattern if args.pattern != "selected" else "")
+                   + ("-reorder" if reorder else ""), "B": wl.B,
                    "H": wl.H, "L": wl.L, "d": wl.d, "block": wl.block, "topk": topk, "n_blocks": nb,
                    "latent": [wl.frames, wl.lat_h, wl.lat_w], "pattern": args.pattern,
                    **({"cube": list(wl.cube)} if cube else {})},
@@ -326,7 +343,7 @@ def main():
                                                       and args.pattern == "selected") else None},
         **({"permute_gbs": round(4 * 2 * wl.B * wl.H * wl.L * row_bytes
                                  / ((t_phase["permute_in"] + t_phase["permute_out"]) * 1e-3) / 1e9, 1)}
-           if cube else {}),
+           if reorder else {}),
         **({"exchange_8bit": quant_err} if quant else {}),
         "timed_wall_s": round(wall, 3),
         "input_gen_s": round(t_gen, 2),

@@ -55,6 +55,13 @@
 // same head as every other XCD at that moment.  All XCDs thus stream the same
 // head's K/V (kept in the shared last-level cache), while each XCD's L2 serves
 // the overlapping selections of its neighbouring query blocks.
+//
+// Cube blocks (3-D boxes of the latent grid, 128 tokens each) are read in place from
+// the frame-major tensors: a tile's 16-byte copies are addressed from the box's first
+// token plus each copy row's offset inside the box (by rows of bx consecutive tokens),
+// which leaves the LDS tile exactly as for 128 consecutive tokens; Q rows, O rows and
+// lse entries likewise sit at their frame-major positions.  No reordered copy of Q, K,
+// V or O is made.
 #include "launchers.h"
 
 namespace sol_attn {
@@ -107,25 +114,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const unsigned char*
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off, int wave,
-                                         int lane) {
+// First token of key/query block j, and offset from it of the block's row r: blocks of
+// 128 consecutive tokens, or boxes of the latent grid read in place (cube blocks).
+template <bool kCube>
+__device__ __forceinline__ int block_first_token(const BoxGeom& g, int j) {
+  return kCube ? g.first_token(j) : j * kBlock;
+}
+template <bool kCube>
+__device__ __forceinline__ int row_token_offset(const BoxGeom& g, int r) {
+  return kCube ? g.row_offset(r) : r;
+}
+
+// Copy one tile (segments wave, wave+8, wave+16, wave+24 of 4 rows each) whose first
+// token starts at byte `off`; rowb[i] = byte offset of this lane's row of segment i.
+__device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off,
+                                         const int (&rowb)[4], int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int seg = wave + 8 * i;
     const int row = 4 * seg + (lane >> 4);
     const int c = (lane & 15) ^ swz(row);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16,
-                                             off + row * 256 + c * 16, 0, 0, 0);
+                                             off + rowb[i] + c * 16, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void tile_dma_seg(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off, int wave,
-                                             int lane, int i) {
+__device__ __forceinline__ void tile_dma_seg(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off,
+                                             const int (&rowb)[4], int wave, int lane, int i) {
   const int seg = wave + 8 * i;
   const int row = 4 * seg + (lane >> 4);
   const int c = (lane & 15) ^ swz(row);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16,
-                                           off + row * 256 + c * 16, 0, 0, 0);
+                                           off + rowb[i] + c * 16, 0, 0, 0);
 }
 
 // Scores of keys past the end of the sequence (a short last key block) -> -inf.
@@ -162,12 +182,13 @@ __device__ __forceinline__ void compute_st(f32x16 (&s)[2], const unsigned char* 
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
 }
 
+template <bool kCube>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
     const unsigned char* __restrict__ v, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ qblock_order, int BH, int L,
     int n_blocks, int topk, int per_xcd, float scale_log2, unsigned char* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, BoxGeom geom) {
   // Four separate LDS arrays (not one): the compiler can then prove that reads of
   // one buffer never alias the in-flight direct-to-LDS copies into another, and
   // does not insert a wait for those copies in the middle of the iteration.
@@ -205,7 +226,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   // ---- Q^T operand: lane holds Q[query n][16*ks + 8*h + 0..7] for ks = 0..7
   // (rows past the end of a short last block load the last row and are not stored)
-  const int qrow = qb * kBlock + qg * 32 + n;
+  const int qrow = block_first_token<kCube>(geom, qb) + row_token_offset<kCube>(geom, qg * 32 + n);
+  // byte offset, from a tile's first token, of this lane's row in each of its copy segments
+  int rowb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rowb[i] = row_token_offset<kCube>(geom, 4 * (wave + 8 * i) + (lane >> 4)) * kD * 2;
+  auto tile_off = [&](int j) { return block_first_token<kCube>(geom, j) * kD * 2; };
   bf16x8 qf[8];
   {
     const unsigned char* qp = q + head_off + (size_t)min(qrow, L - 1) * kD * 2;
@@ -239,16 +265,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   // ---- prologue: K0, K1, K2 and V0 into LDS; S_0
   // K(j) lives in K buffer j%3 and is read in step j-1 (for S_j), V(j) in V buffer j%2,
-  // read in step j.  Step t refills the K buffer of K(t) (read in step t-1) with K(t+3)
-  // and the V buffer of V(t-1) with V(t+1); V is issued first, so the step's closing
-  // wait (vmcnt <= one tile copy) leaves only K(t+3) in flight: K copies get two steps,
-  // V copies one.  Past the end of the list the last tile is copied again into the free
-  // buffer (never read), keeping the number of copies per step fixed.
+  // read in step j.  Step t refills the V buffer of V(t-1) with V(t+1), issued after the
+  // softmax, and the K buffer of K(t) (read in step t-1) with K(t+3), one quarter per
+  // k-step of the P.V products; so V's copies precede K's, and the wait opening step
+  // t+1 (vmcnt <= 4) leaves only this wave's four K(t+3) copies in flight.  Past the end
+  // of the list the last tile is copied again into the free buffer (never read),
+  // keeping the number of copies per step fixed.
   auto blk = [&](int t) { return tile_block(min(t, topk - 1)); };
-  tile_dma(kbuf(0), k_rsrc, blk(0) * kTileBytes, wave, lane);
-  tile_dma(vbuf(0), v_rsrc, blk(0) * kTileBytes, wave, lane);
-  tile_dma(kbuf(1), k_rsrc, blk(1) * kTileBytes, wave, lane);
-  tile_dma(kbuf(2), k_rsrc, blk(2) * kTileBytes, wave, lane);
+  tile_dma(kbuf(0), k_rsrc, tile_off(blk(0)), rowb, wave, lane);
+  tile_dma(vbuf(0), v_rsrc, tile_off(blk(0)), rowb, wave, lane);
+  tile_dma(kbuf(1), k_rsrc, tile_off(blk(1)), rowb, wave, lane);
+  tile_dma(kbuf(2), k_rsrc, tile_off(blk(2)), rowb, wave, lane);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));      // K0 and V0 landed (K1, K2 may fly)
   __syncthreads();
   f32x16 sa[2], sb[2];
@@ -269,12 +296,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int k3_blk = blk(t + 3);
+    const int k3_off = tile_off(blk(t + 3));
     // key half 0 computes the next S first, key half 1 after its softmax
     if (kh == 0 && has_next) compute_st(snext, k_next, key0, qf, n, h);
 
     // softmax on S_t (log2 domain)
-    const int valid = L - this_blk * kBlock;   // keys of the tile that exist (short last block)
+    const int valid = kCube ? kBlock : L - this_blk * kBlock;   // keys that exist (short last block)
     if (valid < kBlock) mask_missing_keys(scur, key0, h, valid);
     float mx = scur[0][0];
 #pragma unroll
@@ -309,13 +336,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
     }
 
-    tile_dma(v_free, v_rsrc, next_blk * kTileBytes, wave, lane);   // V copies after the softmax
+    tile_dma(v_free, v_rsrc, tile_off(next_blk), rowb, wave, lane);   // V copies after the softmax
     if (kh == 1 && has_next) compute_st(snext, k_next, key0, qf, n, h);
 
     // O^T += V^T P^T over this wave's 64 keys
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      tile_dma_seg(k_free, k_rsrc, k3_blk * kTileBytes, wave, lane, ks);   // one K copy per k-step
+      tile_dma_seg(k_free, k_rsrc, k3_off, rowb, wave, lane, ks);   // one K copy per k-step
       const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]});
       const unsigned char* vk = v_cur + ks * 16 * 256;
 #pragma unroll
@@ -395,18 +422,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, int BH, int L, int topk,
-                           const int32_t* block_idx, const int32_t* qblock_order, float scale, void* out,
-                           float* lse, hipStream_t stream) {
+                           const int32_t* block_idx, const int32_t* qblock_order, const BoxGeom* cube,
+                           float scale, void* out, float* lse, hipStream_t stream) {
   (void)hipGetLastError();   // report this launch only, not an earlier unrelated error
   const int n_blocks = (L + kBlock - 1) / kBlock;   // the last block may be short
   const float scale_log2 = scale * 1.4426950408889634f;
   const int per_xcd = (n_blocks + kXcds - 1) / kXcds;
   const long long grid = (long long)kXcds * per_xcd * BH;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fwd_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     static_cast<const unsigned char*>(q), static_cast<const unsigned char*>(k),
-                     static_cast<const unsigned char*>(v), block_idx, qblock_order, BH, L, n_blocks, topk, per_xcd,
-                     scale_log2, static_cast<unsigned char*>(out), lse);
+  const BoxGeom geom = cube ? *cube : BoxGeom{};
+  const auto* qs = static_cast<const unsigned char*>(q);
+  const auto* ks = static_cast<const unsigned char*>(k);
+  const auto* vs = static_cast<const unsigned char*>(v);
+  auto* os = static_cast<unsigned char*>(out);
+  if (cube)
+    hipLaunchKernelGGL(fwd_bf16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, qs, ks, vs,
+                       block_idx, qblock_order, BH, L, n_blocks, topk, per_xcd, scale_log2, os, lse, geom);
+  else
+    hipLaunchKernelGGL(fwd_bf16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, qs, ks, vs,
+                       block_idx, qblock_order, BH, L, n_blocks, topk, per_xcd, scale_log2, os, lse, geom);
   return hipGetLastError();
 }
 

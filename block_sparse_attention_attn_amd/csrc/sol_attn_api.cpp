@@ -68,7 +68,7 @@ int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, 
   if (!aligned(q, 16) || !aligned(k, 16)) return fail(SOL_ATTN_ERR_ALIGN, "pool: q/k not 16-byte aligned");
   if (!aligned(q_pooled, 8) || !aligned(k_pooled, 8))
     return fail(SOL_ATTN_ERR_ALIGN, "pool: pooled outputs not 8-byte aligned");
-  return hip_status(sol_attn::launch_pool(q, k, bf16, (int)BH, L, d, block, q_pooled, k_pooled,
+  return hip_status(sol_attn::launch_pool(q, k, bf16, (int)BH, L, d, block, nullptr, q_pooled, k_pooled,
                                           static_cast<hipStream_t>(stream)),
                     "pool launch");
 }
@@ -109,6 +109,8 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
   const int n_blocks = (int)(((long long)L + block - 1) / block);   // the last block may be short
   if (topk < 1 || topk > n_blocks) return fail(SOL_ATTN_ERR_K, "topk=%d outside [1, n_blocks=%d]", topk, n_blocks);
   if (!bf16 && BH > 65535) return fail(SOL_ATTN_ERR_SHAPE, "fp32 fwd grid too large (B*H must be <= 65535)");
+  if (bf16 && (long long)L * d * 2 > 0x7fffffffLL)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "bf16 fwd needs L*d*2 < 2^31 bytes per head (L=%d)", L);
   if (!q || !k || !v || !block_idx || !out) return fail(SOL_ATTN_ERR_NULL, "fwd: NULL pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(SOL_ATTN_ERR_ALIGN, "fwd: q/k/v/out not 16-byte aligned");
@@ -119,7 +121,7 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (bf16)
     return hip_status(sol_attn::launch_fwd_bf16(q, k, v, (int)BH, L, topk, block_idx, qblock_order_or_null,
-                                                scale, out, lse_or_null, s),
+                                                nullptr, scale, out, lse_or_null, s),
                       "fwd bf16 launch");
   return hip_status(sol_attn::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                              static_cast<const float*>(v), (int)BH, L, d, block, topk,
@@ -150,6 +152,74 @@ int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h
   return hip_status(sol_attn::launch_cube_permute(src, dst, (int)BH, T, h, w, row_bytes, bt, by, bx, inverse == 1,
                                                   static_cast<hipStream_t>(stream)),
                     "cube_permute launch");
+}
+
+namespace {
+
+// The latent grid and box of the cube-block calls; on success *L is T*h*w.
+int check_cube(const char* call, int B, int H, int T, int h, int w, int bt, int by, int bx, long long* L) {
+  if (B < 0 || H < 0 || T < 0 || h < 0 || w < 0)
+    return fail(SOL_ATTN_ERR_SHAPE, "%s: negative size B=%d H=%d T=%d h=%d w=%d", call, B, H, T, h, w);
+  if (bt < 1 || by < 1 || bx < 1 || T % bt || h % by || w % bx)
+    return fail(SOL_ATTN_ERR_SHAPE, "%s: box %dx%dx%d does not tile the %dx%dx%d grid", call, bt, by, bx, T, h, w);
+  *L = (long long)T * h * w;
+  if (*L > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "%s: grid of %lld tokens too large", call, *L);
+  if ((long long)B * H > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "%s: B*H too large", call);
+  return SOL_ATTN_OK;
+}
+
+}  // namespace
+
+int sol_attn_pool_cube(const void* q, const void* k, int dtype, int B, int H, int T, int h, int w, int d, int bt,
+                       int by, int bx, double* q_pooled, double* k_pooled, void* stream) {
+  long long L = 0;
+  int st = check_cube("pool_cube", B, H, T, h, w, bt, by, bx, &L);
+  if (st != SOL_ATTN_OK) return st;
+  const long long V = (long long)bt * by * bx;
+  if (V > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "pool_cube: box of %lld tokens too large", V);
+  st = check_common(dtype, B, H, (int)L, d, (int)V);
+  if (st != SOL_ATTN_OK) return st;
+  const bool bf16 = dtype == SOL_ATTN_BF16;
+  if (d > 512 || d % (bf16 ? 8 : 4) != 0)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "pool_cube needs d <= 512 and d %% %d == 0 (d=%d)", bf16 ? 8 : 4, d);
+  const long long BH = (long long)B * H;
+  if (BH * L == 0) return ok();
+  if (BH > 65535) return fail(SOL_ATTN_ERR_SHAPE, "pool_cube grid too large (B*H must be <= 65535)");
+  if (!q || !k || !q_pooled || !k_pooled) return fail(SOL_ATTN_ERR_NULL, "pool_cube: NULL pointer");
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(SOL_ATTN_ERR_ALIGN, "pool_cube: q/k not 16-byte aligned");
+  if (!aligned(q_pooled, 8) || !aligned(k_pooled, 8))
+    return fail(SOL_ATTN_ERR_ALIGN, "pool_cube: pooled outputs not 8-byte aligned");
+  const sol_attn::BoxGeom g = sol_attn::make_box_geom(h, w, bt, by, bx);
+  return hip_status(sol_attn::launch_pool(q, k, bf16, (int)BH, (int)L, d, (int)V, &g, q_pooled, k_pooled,
+                                          static_cast<hipStream_t>(stream)),
+                    "pool_cube launch");
+}
+
+int sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H, int T, int h, int w, int bt, int by,
+                      int bx, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                      float softmax_scale, void* out, float* lse_or_null, void* stream) {
+  long long L = 0;
+  int st = check_cube("fwd_cube", B, H, T, h, w, bt, by, bx, &L);
+  if (st != SOL_ATTN_OK) return st;
+  if ((long long)bt * by * bx != 128)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "fwd_cube needs boxes of 128 tokens (box %dx%dx%d)", bt, by, bx);
+  const long long BH = (long long)B * H;
+  if (BH * L == 0) return ok();
+  if (L * 128 * 2 > 0x7fffffffLL)
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "fwd_cube needs T*h*w*256 < 2^31 bytes per head (%lld tokens)", L);
+  const int n_blocks = (int)(L / 128);
+  if (topk < 1 || topk > n_blocks) return fail(SOL_ATTN_ERR_K, "topk=%d outside [1, n_blocks=%d]", topk, n_blocks);
+  if (!q || !k || !v || !block_idx || !out) return fail(SOL_ATTN_ERR_NULL, "fwd_cube: NULL pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(SOL_ATTN_ERR_ALIGN, "fwd_cube: q/k/v/out not 16-byte aligned");
+  if (!aligned(block_idx, 4) || (lse_or_null && !aligned(lse_or_null, 4)) ||
+      (qblock_order_or_null && !aligned(qblock_order_or_null, 4)))
+    return fail(SOL_ATTN_ERR_ALIGN, "fwd_cube: block_idx/qblock_order/lse not 4-byte aligned");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+  const sol_attn::BoxGeom g = sol_attn::make_box_geom(h, w, bt, by, bx);
+  return hip_status(sol_attn::launch_fwd_bf16(q, k, v, (int)BH, (int)L, topk, block_idx, qblock_order_or_null, &g,
+                                              scale, out, lse_or_null, static_cast<hipStream_t>(stream)),
+                    "fwd_cube launch");
 }
 
 namespace {

@@ -64,6 +64,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sol_attn_window_blocks.argtypes = [i, i, vp]
     lib.sol_attn_window_blocks.restype = i
     lib.sol_attn_cube_permute.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, i, vp]
+    lib.sol_attn_pool_cube.restype = i
+    lib.sol_attn_pool_cube.argtypes = [vp, vp, i, i, i, i, i, i, i, i, i, i, vp, vp, vp]
+    lib.sol_attn_fwd_cube.restype = i
+    lib.sol_attn_fwd_cube.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.sol_attn_cube_permute.restype = i
     lib.sol_attn_quantize.argtypes = [vp, i, i, i, i, i, vp, vp, vp]
     lib.sol_attn_quantize.restype = i
@@ -238,24 +242,89 @@ def sol_attn_cube_permute(x: torch.Tensor, grid: Tuple[int, int, int], cube: Tup
     return out
 
 
+def _check_grid(L: int, grid: Tuple[int, int, int]):
+    T, h, w = grid
+    if T * h * w != L:
+        raise ValueError(f"grid {grid} does not hold L={L} tokens")
+
+
+def sol_attn_pool_cube(q: torch.Tensor, k: torch.Tensor, grid: Tuple[int, int, int],
+                       cube: Tuple[int, int, int]) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Mean of every bt x by x bx box of frame-major q, k ([B,H,T*h*w,d]), read in place:
+    float64 [B,H,n_boxes,d] with boxes numbered time, row, column."""
+    lib = load_library()
+    _check_qkv(q, k)
+    B, H, L, d = q.shape
+    _check_grid(L, grid)
+    T, h, w = grid
+    bt, by, bx = cube
+    nb = (T // bt) * (h // by) * (w // bx) if min(bt, by, bx) > 0 else 0
+    qp = torch.empty((B, H, nb, d), dtype=torch.float64, device=q.device)
+    kp = torch.empty_like(qp)
+    _check("sol_attn_pool_cube", lib.sol_attn_pool_cube(_ptr(q), _ptr(k), _dtype_code(q), B, H, T, h, w, d, bt, by,
+                                                        bx, _ptr(qp), _ptr(kp), _stream(q)))
+    return qp, kp
+
+
+def sol_attn_fwd_cube(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor,
+                      grid: Tuple[int, int, int], cube: Tuple[int, int, int], softmax_scale: Optional[float] = None,
+                      return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                      qblock_order: Optional[torch.Tensor] = None):
+    """bf16 sparse attention (d = 128) with query/key block c = box c (128 tokens) of the
+    frame-major latent grid, read and written in place."""
+    lib = load_library()
+    _check_qkv(q, k, v)
+    B, H, L, d = q.shape
+    _check_grid(L, grid)
+    T, h, w = grid
+    bt, by, bx = cube
+    if block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4:
+        raise ValueError("block_idx must be contiguous int32 [B,H,n_boxes,topk]")
+    nb = L // (bt * by * bx) if min(bt, by, bx) > 0 else 0
+    if tuple(block_idx.shape[:3]) != (B, H, nb):
+        raise ValueError("block_idx leading dims must be [B,H,n_boxes]")
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
+    if qblock_order is not None:
+        if (qblock_order.dtype != torch.int32 or qblock_order.device != q.device or qblock_order.numel() != nb
+                or not qblock_order.is_contiguous()):
+            raise ValueError("qblock_order must be a contiguous int32 device tensor of n_boxes entries")
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check("sol_attn_fwd_cube", lib.sol_attn_fwd_cube(_ptr(q), _ptr(k), _ptr(v), B, H, T, h, w, bt, by, bx,
+                                                      block_idx.shape[-1], _ptr(block_idx), _ptr(qblock_order),
+                                                      scale, _ptr(out), _ptr(lse), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
 def cube_sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Tuple[int, int, int],
                           cube: Tuple[int, int, int], topk: int, softmax_scale: Optional[float] = None,
-                          return_lse: bool = False, return_idx: bool = False):
-    """Sparse attention with 3-D cube blocks on frame-major q, k, v: reorder to cube-major,
-    pool -> select -> fwd with block = bt*by*bx, reorder the outputs back.  block_idx (if
-    returned) indexes boxes in cube-major numbering."""
+                          return_lse: bool = False, return_idx: bool = False, reorder: bool = False):
+    """Sparse attention with 3-D cube blocks on frame-major q, k, v.  block_idx (if
+    returned) indexes boxes in cube-major numbering.
+
+    bf16 with 128-token boxes and d = 128 reads the boxes in place (pool_cube,
+    select, fwd_cube); otherwise, or with reorder=True, q, k, v are reordered to
+    cube-major order, pooled, selected and attended with block = bt*by*bx, and the
+    outputs reordered back.  Both routes give the same bits."""
     T, h, w = grid
     bt, by, bx = cube
     V = bt * by * bx
-    qc, kc, vc = (sol_attn_cube_permute(x, grid, cube) for x in (q, k, v))
-    qp, kp = sol_attn_pool(qc, kc, V)
-    idx = sol_attn_select(qp, kp, topk)
     order = sol_attn_frame_order(q.shape[2], V, V * (h // by) * (w // bx), V * (w // bx)).to(q.device)
-    res = sol_attn_fwd(qc, kc, vc, idx, V, softmax_scale, return_lse, qblock_order=order)
-    oc, lc = res if return_lse else (res, None)
-    out = [sol_attn_cube_permute(oc, grid, cube, inverse=True)]
-    if return_lse:
-        out.append(sol_attn_cube_permute(lc, grid, cube, inverse=True))
+    if not reorder and q.dtype == torch.bfloat16 and V == 128 and q.shape[-1] == 128:
+        qp, kp = sol_attn_pool_cube(q, k, grid, cube)
+        idx = sol_attn_select(qp, kp, topk)
+        res = sol_attn_fwd_cube(q, k, v, idx, grid, cube, softmax_scale, return_lse, qblock_order=order)
+        out = list(res) if return_lse else [res]
+    else:
+        qc, kc, vc = (sol_attn_cube_permute(x, grid, cube) for x in (q, k, v))
+        qp, kp = sol_attn_pool(qc, kc, V)
+        idx = sol_attn_select(qp, kp, topk)
+        res = sol_attn_fwd(qc, kc, vc, idx, V, softmax_scale, return_lse, qblock_order=order)
+        oc, lc = res if return_lse else (res, None)
+        out = [sol_attn_cube_permute(oc, grid, cube, inverse=True)]
+        if return_lse:
+            out.append(sol_attn_cube_permute(lc, grid, cube, inverse=True))
     if return_idx:
         out.append(idx)
     return out[0] if len(out) == 1 else tuple(out)

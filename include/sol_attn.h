@@ -20,7 +20,8 @@
  *                    softmax(q k^T * scale) over the tokens of its selected key
  *                    blocks only; no mask.
  *
- * Around them: sol_attn_cube_permute (3-D cube blocks instead of runs of tokens),
+ * Around them: sol_attn_cube_permute, sol_attn_pool_cube and sol_attn_fwd_cube (3-D
+ * cube blocks instead of runs of tokens),
  * sol_attn_window_blocks (a static windowed pattern for sol_attn_fwd),
  * sol_attn_check_block_idx (device check of an index list), sol_attn_frame_order (a
  * cache-friendly query-block schedule), sol_attn_quantize / sol_attn_dequantize (the
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SOL_ATTN_VERSION 101  /* major*100 + minor */
+#define SOL_ATTN_VERSION 102  /* major*100 + minor */
 
 typedef enum {
   SOL_ATTN_BF16 = 0,  /* bfloat16 inputs/outputs, float32 accumulation */
@@ -188,7 +189,8 @@ int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
  *      tensors (block_idx then indexes boxes);
  *   3. cube_permute O (and lse, with row_bytes = 4) back with inverse = 1.
  * A model whose token-wise layers do not care about order can keep its activations in
- * cube-major order and skip steps 1 and 3.
+ * cube-major order and skip steps 1 and 3.  sol_attn_pool_cube and sol_attn_fwd_cube
+ * (below) do steps 1-3 without the copies, reading the frame-major tensors in place.
  *   src, dst    [B,H,T*h*w] rows of row_bytes bytes each (a [B,H,L,d] tensor has
  *               row_bytes = d * element size); must not overlap; 4-byte aligned (16-byte
  *               alignment and bx*row_bytes % 16 == 0 select 16-byte accesses).
@@ -198,6 +200,35 @@ int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
  */
 int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
                           int by, int bx, int inverse, void* stream);
+
+/*
+ * Cube blocks read in place: sol_attn_pool with the blocks replaced by the bt x by x bx
+ * boxes of the frame-major T x h x w latent grid (boxes numbered time, row, column as
+ * for sol_attn_cube_permute; block c of the output is box c).  q, k stay frame-major
+ * [B,H,T*h*w,d]; no reordered copy is made.  The pooled values equal those of
+ * sol_attn_pool on the cube_permute'd tensors with block = bt*by*bx, bit for bit.
+ *   q_pooled, k_pooled  float64 [B,H,n_boxes,d], n_boxes = (T/bt)*(h/by)*(w/bx).
+ * Errors: as sol_attn_cube_permute for the grid and box (SOL_ATTN_ERR_SHAPE), then as
+ * sol_attn_pool for dtype, d, B*H, NULL and alignment.
+ */
+int sol_attn_pool_cube(const void* q, const void* k, int dtype, int B, int H, int T, int h, int w, int d, int bt,
+                       int by, int bx, double* q_pooled, double* k_pooled, void* stream);
+
+/*
+ * Cube blocks read in place: the bf16 sol_attn_fwd (d = 128) with query and key block
+ * c = box c of the frame-major latent grid, which must hold 128 tokens
+ * (bt*by*bx == 128).  q, k, v, out [B,H,T*h*w,128] bf16 and lse [B,H,T*h*w] stay
+ * frame-major; every output row is written (boxes tile the grid).  block_idx
+ * [B,H,n_boxes,topk] indexes boxes, strictly ascending per row as for sol_attn_fwd;
+ * qblock_order_or_null orders boxes.  The results equal those of sol_attn_fwd on the
+ * cube_permute'd tensors, permuted back, bit for bit.
+ * Errors: SOL_ATTN_ERR_SHAPE for the grid and box as sol_attn_cube_permute;
+ * SOL_ATTN_ERR_UNSUPPORTED for a box of other than 128 tokens or a head of 2^31 bytes
+ * or more; then as sol_attn_fwd.
+ */
+int sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H, int T, int h, int w, int bt, int by,
+                      int bx, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                      float softmax_scale, void* out, float* lse_or_null, void* stream);
 
 /*
  * 8-bit exchange formats.  Between GPUs the Sol-H3 runtime sends Q, K and V as INT8 and

@@ -22,14 +22,15 @@ def test_header_symbols_exported(lib):
     assert set(names) == {"sol_attn_pool", "sol_attn_select", "sol_attn_fwd", "sol_attn_last_error",
                           "sol_attn_version", "sol_attn_frame_order", "sol_attn_window_blocks",
                           "sol_attn_cube_permute", "sol_attn_quantize", "sol_attn_dequantize",
-                          "sol_attn_check_block_idx", "sol_attn_probe_mfma"}
+                          "sol_attn_check_block_idx", "sol_attn_probe_mfma", "sol_attn_pool_cube",
+                          "sol_attn_fwd_cube"}
     raw = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version(lib):
-    assert lib.sol_attn_version() == 101
+    assert lib.sol_attn_version() == 102
 
 
 FAKE = 0x10000      # 64 KiB-aligned dummy "device" address; never dereferenced
@@ -144,6 +145,43 @@ def test_cube_permute_argument_checks(lib):
     assert _perm(lib, H=0, src=None) == 0              # nothing to do
     assert _perm(lib, T=0, h=0, w=0) == 0
     assert b"does not tile" in (_perm(lib, by=3), lib.sol_attn_last_error())[1]
+
+
+def test_pool_cube_argument_checks(lib):
+    def p(q=FAKE, k=FAKE, dtype=0, B=1, H=1, T=4, h=16, w=16, d=128, bt=2, by=8, bx=8, qp=FAKE, kp=FAKE):
+        return lib.sol_attn_pool_cube(q, k, dtype, B, H, T, h, w, d, bt, by, bx, qp, kp, None)
+    assert p(T=-1) == 2
+    assert p(bt=3) == 2                        # box does not divide T
+    assert p(bx=0) == 2
+    assert p(dtype=5) == 4
+    assert p(d=12) == 4                        # bf16 pool needs d % 8 == 0
+    assert p(B=65536) == 2
+    assert p(q=None) == 1
+    assert p(k=MIS) == 5
+    assert p(kp=FAKE + 4) == 5
+    assert p(H=0, q=None) == 0                 # nothing to do
+    assert b"does not tile" in (p(by=3), lib.sol_attn_last_error())[1]
+
+
+def test_fwd_cube_argument_checks(lib):
+    def f(q=FAKE, k=FAKE, v=FAKE, B=1, H=1, T=4, h=16, w=16, bt=2, by=8, bx=8, topk=2, idx=FAKE, order=None,
+          out=FAKE, lse=None):
+        return lib.sol_attn_fwd_cube(q, k, v, B, H, T, h, w, bt, by, bx, topk, idx, order, 0.0, out, lse, None)
+    assert f(h=-16) == 2
+    assert f(by=3) == 2                        # box does not divide h
+    assert f(bt=1, by=4, bx=4) == 4            # 16-token boxes: needs 128
+    assert f(bt=4, by=8, bx=8) == 4            # 256-token boxes
+    assert f(T=1024, h=256, w=256, bt=2) == 4  # a head of 2^31 bytes or more
+    assert f(topk=0) == 3
+    assert f(topk=9) == 3                      # 8 boxes
+    assert f(v=None) == 1
+    assert f(idx=None) == 1
+    assert f(out=MIS) == 5
+    assert f(lse=FAKE + 2) == 5
+    assert f(order=FAKE + 1) == 5
+    assert f(B=0, q=None, idx=None) == 0       # nothing to do
+    assert f(T=0, topk=99) == 0
+    assert lib.sol_attn_last_error() == b""
 
 
 def test_quantize_argument_checks(lib):

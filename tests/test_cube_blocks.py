@@ -249,3 +249,62 @@ def test_cube_path_full_size():
         errs.append(np.abs(o[bh, torch.from_numpy(rows)].double().cpu().numpy() - Oh[rows]))
     err = np.concatenate(errs)
     assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape,grid,cube,dtype", [
+    ((1, 2, 1024, 128), (4, 16, 16), (2, 8, 8), "bf16"),
+    ((1, 2, 4096, 128), (4, 32, 32), (4, 8, 4), "bf16"),
+    ((2, 1, 240, 64), (4, 6, 10), (2, 3, 5), "fp32"),       # 30-token boxes
+    ((1, 2, 1024, 64), (4, 16, 16), (4, 4, 4), "fp32"),
+])
+def test_pool_cube_reads_the_boxes_in_place(shape, grid, cube, dtype):
+    """Box means read from frame-major tensors: close to the oracle's exact (fsum)
+    means, and bit-identical to pooling the reordered tensors with block = box volume."""
+    S = _gpu_lib()
+    q, k = _rand(shape, 41), _rand(shape, 42)
+    if dtype == "bf16":
+        from block_sparse_attention_attn_amd.workloads import f64_to_bf16_bits
+        q, k = (f64_to_bf16_bits(x) for x in (q, k))
+    else:
+        q, k = q.astype(np.float32), k.astype(np.float32)
+    Q, K = _dev(q, dtype), _dev(k, dtype)
+    qp, kp = S.sol_attn_pool_cube(Q, K, grid, cube)
+    qc, kc = (S.sol_attn_cube_permute(x, grid, cube) for x in (Q, K))
+    qr, kr = S.sol_attn_pool(qc, kc, int(np.prod(cube)))
+    torch.cuda.synchronize()
+    assert torch.equal(qp, qr) and torch.equal(kp, kr)
+    sets = oracle.cube_blocks(*grid, cube)
+    for x, got in ((q, qp), (k, kp)):
+        want = oracle.pool_sets(oracle.widen(x, dtype), sets)
+        assert np.abs(got.cpu().numpy() - want).max() <= 1e-12
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,H,grid,cube,topk", [
+    (1, 2, (4, 16, 16), (2, 8, 8), 1),
+    (1, 2, (4, 16, 16), (2, 8, 8), 5),
+    (2, 1, (4, 32, 32), (4, 8, 4), 7),
+    (1, 1, (8, 16, 64), (1, 8, 16), 12),     # boxes of 8 runs of 16 tokens
+    (1, 1, (2, 8, 128), (1, 1, 128), 3),     # boxes that are whole latent rows
+])
+def test_fwd_cube_equals_the_reordering_route(B, H, grid, cube, topk):
+    """The in-place route (pool_cube, select, fwd_cube) and the reordering route
+    (cube_permute, pool, select, fwd, permute back) give the same bits: the kernel reads
+    the same 128 token rows into the same tile rows either way."""
+    from block_sparse_attention_attn_amd.workloads import f64_to_bf16_bits
+    S = _gpu_lib()
+    L = int(np.prod(grid))
+    q, k, v = (f64_to_bf16_bits(_rand((B, H, L, 128), 60 + i)) for i in range(3))
+    Q, K, V = (_dev(x, "bf16") for x in (q, k, v))
+    a = S.cube_sparse_attention(Q, K, V, grid, cube, topk, return_lse=True, return_idx=True)
+    b = S.cube_sparse_attention(Q, K, V, grid, cube, topk, return_lse=True, return_idx=True, reorder=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[2], b[2])
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+    ref = oracle.run_cube(q, k, v, "bf16", grid, cube, topk)
+    assert np.array_equal(a[2].cpu().numpy(), ref["idx"])
+    err = np.abs(a[0].double().cpu().numpy() - ref["out"])
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+    assert np.abs(a[1].double().cpu().numpy() - ref["lse"]).max() <= 1e-2
