@@ -259,8 +259,9 @@ def test_cube_path_full_size():
     ((1, 2, 1024, 64), (4, 16, 16), (4, 4, 4), "fp32"),
 ])
 def test_pool_cube_reads_the_boxes_in_place(shape, grid, cube, dtype):
-    """Box means read from frame-major tensors: close to the oracle's exact (fsum)
-    means, and bit-identical to pooling the reordered tensors with block = box volume."""
+    """Box means read from frame-major tensors: bit-identical to pooling the reordered
+    tensors with block = box volume, and to the oracle's means for bf16 (a float64 sum of
+    at most 128 bf16 values is exact in any order); within 1e-12 for float32 inputs."""
     S = _gpu_lib()
     q, k = _rand(shape, 41), _rand(shape, 42)
     if dtype == "bf16":
@@ -277,7 +278,10 @@ def test_pool_cube_reads_the_boxes_in_place(shape, grid, cube, dtype):
     sets = oracle.cube_blocks(*grid, cube)
     for x, got in ((q, qp), (k, kp)):
         want = oracle.pool_sets(oracle.widen(x, dtype), sets)
-        assert np.abs(got.cpu().numpy() - want).max() <= 1e-12
+        if dtype == "bf16":
+            assert np.array_equal(got.cpu().numpy(), want)
+        else:
+            assert np.abs(got.cpu().numpy() - want).max() <= 1e-12
 
 
 @pytest.mark.gpu
