@@ -38,8 +38,10 @@
 // for this wave's copies the iteration reads, leaving the youngest K copy in flight;
 // copies spread through the iteration instead of issued in one burst at its start
 // run 5-7 % faster at the 1344x768 size (they slow the LDS reads of the products
-// less).  The iterations are unrolled six at a time (periods 3 and 2), so every
-// buffer is a compile-time choice and the compiler adds no waits of its own.  The
+// less).  The byte offsets of a step's copies are computed during the previous
+// step's products (scalar work off the top of the step: 0.5 %).  The iterations are
+// unrolled six at a time (periods 3 and 2), so every buffer is a compile-time choice
+// and the compiler adds no waits of its own.  The
 // two key-half waves that share a SIMD run the S product and the softmax in
 // opposite order, so one wave's softmax (VALU, exp) overlaps the other's
 // matrix-core work.
@@ -282,6 +284,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   compute_st(sa, kbuf(0), key0, qf, n, h);
 
   int cur_blk = blk(0);   // block of tile t, read (scalar) by the step before: no vector load in the loop
+  // byte offsets of the tiles a step copies (V(t+1), K(t+3)), computed during the
+  // previous step's products rather than at the top of the step
+  int v_next_off = tile_off(blk(1)), k3_next_off = tile_off(blk(3));
   auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int t, unsigned char* k_next, unsigned char* k_free,
                   unsigned char* v_cur, unsigned char* v_free) __attribute__((always_inline)) {
     const bool has_next = t + 1 < topk;
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int k3_off = tile_off(blk(t + 3));
+    const int k3_off = k3_next_off, v_off = v_next_off;
     // key half 0 computes the next S first, key half 1 after its softmax
     if (kh == 0 && has_next) compute_st(snext, k_next, key0, qf, n, h);
 
@@ -336,13 +341,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
     }
 
-    tile_dma(v_free, v_rsrc, tile_off(next_blk), rowb, wave, lane);   // V copies after the softmax
+    tile_dma(v_free, v_rsrc, v_off, rowb, wave, lane);   // V copies after the softmax
     if (kh == 1 && has_next) compute_st(snext, k_next, key0, qf, n, h);
 
     // O^T += V^T P^T over this wave's 64 keys
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       tile_dma_seg(k_free, k_rsrc, k3_off, rowb, wave, lane, ks);   // one K copy per k-step
+      if (ks == 0) {
+        v_next_off = tile_off(blk(t + 2));
+        k3_next_off = tile_off(blk(t + 4));
+      }
       const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]});
       const unsigned char* vk = v_cur + ks * 16 * 256;
 #pragma unroll
