@@ -164,24 +164,26 @@ __device__ __forceinline__ void mask_missing_keys(f32x16 (&s)[2], int key0, int 
 // S^T (64 keys of this wave's half x 32 queries) = K_half . Q^T.
 __device__ __forceinline__ void compute_st(f32x16 (&s)[2], const unsigned char* kt, int key0,
                                            const bf16x8 (&qf)[8], int n, int h) {
+  // the two 32-key accumulators alternate, so consecutive products are independent
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    s[mb] = f32x16{};
-    const int row = key0 + 32 * mb + n;
+  for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = key0 + 32 * mb + n;
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + lds_off(row, 2 * ks + h));
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
     }
   }
-  // keep at most two operand reads ahead of the matrix core (bounds register use)
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  // operand reads run four products ahead of the matrix core (deeper costs registers)
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < 12; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
 }
 
 template <bool kCube>
@@ -363,13 +365,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[md], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+    // transposed V reads run three products ahead (two reads per product)
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < 13; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 1);
   };
 
   // six steps per round: K buffers cycle with period 3, V buffers and S registers with 2
