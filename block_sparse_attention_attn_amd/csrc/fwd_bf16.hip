@@ -41,10 +41,11 @@
 // less).  The byte offsets of a step's copies are computed during the previous
 // step's products (scalar work off the top of the step: 0.5 %).  The iterations are
 // unrolled six at a time (periods 3 and 2), so every buffer is a compile-time choice
-// and the compiler adds no waits of its own.  The
-// two key-half waves that share a SIMD run the S product and the softmax in
-// opposite order, so one wave's softmax (VALU, exp) overlaps the other's
-// matrix-core work.
+// and the compiler adds no waits of its own.  Operand reads run ahead of the
+// products: K four products ahead (the two 32-key S accumulators alternate), V three
+// (two transposed reads each).  The two key-half waves that share a SIMD run the S
+// product and the softmax in opposite order, so one wave's softmax (VALU, exp)
+// overlaps the other's matrix-core work.
 //
 // LDS layout of a 128x128 bf16 tile: row r = 256 bytes = 16 chunks of 16 bytes;
 // logical chunk c lives at physical chunk c ^ swz(r), swz(r) = 4*(r%4) + (r/4)%4.
