@@ -8,7 +8,8 @@ H=40, d=128, bf16, 128-token blocks, top-76 of 504 key blocks).
 Prints ONE JSON line.  `value` = effective TFLOP/s of the whole step, counting the
 two contractions over the selected key blocks only (4*B*H*L*k*Bs*d flops per step).
 `roofline` covers the dominant kernel (sol_attn_fwd): algorithmic flops per launch
-divided by its average launch time measured with HIP events on its stream.
+divided by its average launch time, from HIP events recorded on its stream between
+the kernels of every timed step.
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -198,7 +199,7 @@ def main():
         for src, dst in ((Q, Qc), (K, Kc), (V, Vc)):
             permute(src, dst, False)
 
-    # the phases of one step, timed one by one in a separate pass
+    # the phases of one step (HIP events between them give per-kernel durations)
     if window:      # static pattern: the step is the attention alone
         phases = [("fwd", run_fwd)]
     elif reorder:
@@ -273,22 +274,19 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, bracketed by synchronisation
+    # timed region: exactly K steps, bracketed by synchronisation; HIP events on the
+    # launch stream between the kernels of every step give the per-kernel durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for e in evs:
+        step(e)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
-
-    # per-kernel durations (separate pass, events between the three launches)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
     samples = {name: np.array([e[n].elapsed_time(e[n + 1]) for e in evs]) for n, (name, _) in enumerate(phases)}
     t_phase = {name: float(np.mean(x)) for name, x in samples.items()}
     t_pool, t_sel, t_fwd = t_phase.get("pool"), t_phase.get("select"), t_phase["fwd"]
