@@ -231,7 +231,7 @@ def test_cube_path_full_size():
     q, k, v = W.make_qkv(wl)
     sets = oracle.cube_blocks(*wl.grid, wl.cube)
     Q, K, V = _dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16")
-    out, idx = S.cube_sparse_attention(Q, K, V, wl.grid, wl.cube, wl.topk, return_idx=True)
+    out, lse, idx = S.cube_sparse_attention(Q, K, V, wl.grid, wl.cube, wl.topk, return_lse=True, return_idx=True)
     torch.cuda.synchronize()
     Qd, Kd, Vd = (oracle.widen(x, "bf16") for x in (q, k, v))
     want_idx = oracle.select(oracle.pool_sets(Qd, sets), oracle.pool_sets(Kd, sets), wl.topk)
@@ -240,15 +240,18 @@ def test_cube_path_full_size():
     o = out.view(-1, wl.L, wl.d)
     Qd, Kd, Vd = (x.reshape(-1, wl.L, wl.d) for x in (Qd, Kd, Vd))
     rng = np.random.default_rng(7)
-    errs = []
+    lh = lse.view(-1, wl.L)
+    errs, lerrs = [], []
     sel = want_idx.reshape(-1, nb, wl.topk)
     for bh in rng.choice(wl.B * wl.H, 3, replace=False):
         blocks = [0, nb - 1] + list(rng.choice(nb, 2, replace=False))
-        Oh, _ = oracle.attend_sets(Qd[bh], Kd[bh], Vd[bh], sets, sel[bh], qblocks=blocks)
-        rows = sets[blocks].reshape(-1)
-        errs.append(np.abs(o[bh, torch.from_numpy(rows)].double().cpu().numpy() - Oh[rows]))
-    err = np.concatenate(errs)
+        Oh, Lh = oracle.attend_sets(Qd[bh], Kd[bh], Vd[bh], sets, sel[bh], qblocks=blocks)
+        rows = torch.from_numpy(sets[blocks].reshape(-1))
+        errs.append(np.abs(o[bh, rows].double().cpu().numpy() - Oh[rows.numpy()]))
+        lerrs.append(np.abs(lh[bh, rows].double().cpu().numpy() - Lh[rows.numpy()]))
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
     assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+    assert lerr.max() <= 1e-2, lerr.max()
 
 
 @pytest.mark.gpu
@@ -291,6 +294,7 @@ def test_pool_cube_reads_the_boxes_in_place(shape, grid, cube, dtype):
     (2, 1, (4, 32, 32), (4, 8, 4), 7),
     (1, 1, (8, 16, 64), (1, 8, 16), 12),     # boxes of 8 runs of 16 tokens
     (1, 1, (2, 8, 128), (1, 1, 128), 3),     # boxes that are whole latent rows
+    (1, 2, (4, 16, 16), (2, 8, 8), 8),       # k = every box: dense attention
 ])
 def test_fwd_cube_equals_the_reordering_route(B, H, grid, cube, topk):
     """The in-place route (pool_cube, select, fwd_cube) and the reordering route
