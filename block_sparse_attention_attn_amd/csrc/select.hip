@@ -100,10 +100,10 @@ __device__ __forceinline__ void topk_rows(const uint64_t* keys, int n_blocks, in
 
 // Same as topk_rows, with each lane's keys (at most MAXPL) cached in registers,
 // so the 64 bisection steps touch no memory.
-template <int MAXPL>
+template <int MAXPL, int NW>
 __device__ __forceinline__ void topk_rows_reg(const uint64_t* keys, int n_blocks, int topk, int nrows,
                                               int wave, int lane, int32_t* __restrict__ out_rows) {
-  for (int r = wave; r < nrows; r += kWaves) {
+  for (int r = wave; r < nrows; r += NW) {
     const uint64_t* rk = keys + (size_t)r * n_blocks;
     uint64_t x[MAXPL];
 #pragma unroll
@@ -218,8 +218,10 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 // lane's S doubles of Qbar and Kbar are read with unconditional 16-byte loads (rows
 // clamped into range) and the next key tile is prefetched while the current one runs
 // through the matrix cores.  kS = 0: any d <= 128, element-wise guarded loads.
-template <int MAXPL, int kS>
-__global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __restrict__ q_pooled,
+// NW waves per workgroup: wave w scores key tiles w, w + NW, ... and then finds the
+// top k of rows w, w + NW, ... of the 16.
+template <int MAXPL, int kS, int NW>
+__global__ __launch_bounds__(NW * 64) void select_mfma_kernel(const double* __restrict__ q_pooled,
                                                                const double* __restrict__ k_pooled,
                                                                int n_blocks, int d, int topk,
                                                                int32_t* __restrict__ block_idx,
@@ -267,10 +269,10 @@ __global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __r
     };
     int j0 = wave * 16;
     if (j0 < n_blocks) load_keys(j0, nb);
-    for (; j0 < n_blocks; j0 += kWaves * 16) {
+    for (; j0 < n_blocks; j0 += NW * 16) {
 #pragma unroll
       for (int t = 0; t < kV; ++t) b[t] = nb[t];
-      if (j0 + kWaves * 16 < n_blocks) load_keys(j0 + kWaves * 16, nb);
+      if (j0 + NW * 16 < n_blocks) load_keys(j0 + NW * 16, nb);
       f64x4 c = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int s = 0; s < kS; ++s) c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s / 2][s % 2], b[s / 2][s % 2], c, 0, 0, 0);
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __r
     double a[kMaxS];
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) a[s] = (s < S && e0 + s < d && col < nrows) ? qr[s] : 0.0;
-    for (int j0 = wave * 16; j0 < n_blocks; j0 += kWaves * 16) {
+    for (int j0 = wave * 16; j0 < n_blocks; j0 += NW * 16) {
       const int j = j0 + col;
       const double* kr = kbase + (size_t)min(j, n_blocks - 1) * d + e0;
       f64x4 c = {0.0, 0.0, 0.0, 0.0};
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void select_mfma_kernel(const double* __r
     }
   }
   __syncthreads();
-  topk_rows_reg<MAXPL>(keys, n_blocks, topk, nrows, wave, lane, block_idx + ((size_t)bh * n_blocks + i0) * topk);
+  topk_rows_reg<MAXPL, NW>(keys, n_blocks, topk, nrows, wave, lane, block_idx + ((size_t)bh * n_blocks + i0) * topk);
 }
 
 template <int kS>
@@ -303,11 +305,17 @@ hipError_t launch_select_mfma(const double* q_pooled, const double* k_pooled, in
                               int topk, int32_t* block_idx, double* scores_or_null, hipStream_t stream) {
   const size_t lds = (size_t)kMfmaRows * n_blocks * 8;
   const int per_lane = (n_blocks + 63) / 64;
-  // keys cached per lane in the top-k phase: the smallest instantiation that holds them
-  auto kern = per_lane <= 4 ? select_mfma_kernel<4, kS>
-            : per_lane <= 8 ? select_mfma_kernel<8, kS>
-            : per_lane <= 16 ? select_mfma_kernel<16, kS>
-            : select_mfma_kernel<(kMaxMfmaBlocks + 63) / 64, kS>;
+  // keys cached per lane in the top-k phase: the smallest instantiation that holds them.
+  // Key rows of more than 80 KiB leave room for one workgroup per CU: it then runs 8
+  // waves instead of 4 (2 per SIMD), which hides the latencies of both phases (2K:
+  // 0.78 -> 0.65 ms); below that two 4-wave workgroups share a CU, which is faster.
+  // (per_lane <= 8 means at most 64 KiB, never wide; per_lane > 16 always is)
+  const bool wide = lds > 80 * 1024;
+  auto kern = per_lane <= 4 ? select_mfma_kernel<4, kS, 4>
+            : per_lane <= 8 ? select_mfma_kernel<8, kS, 4>
+            : per_lane <= 16 ? (wide ? select_mfma_kernel<16, kS, 8> : select_mfma_kernel<16, kS, 4>)
+            : select_mfma_kernel<(kMaxMfmaBlocks + 63) / 64, kS, 8>;
+  const int threads = wide ? 8 * 64 : 4 * 64;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) {
@@ -315,7 +323,7 @@ hipError_t launch_select_mfma(const double* q_pooled, const double* k_pooled, in
     return err;
   }
   dim3 grid((n_blocks + kMfmaRows - 1) / kMfmaRows, BH);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, q_pooled, k_pooled, n_blocks, d, topk, block_idx,
+  hipLaunchKernelGGL(kern, grid, dim3(threads), lds, stream, q_pooled, k_pooled, n_blocks, d, topk, block_idx,
                      scores_or_null, sqrt((double)d));
   return hipGetLastError();
 }
