@@ -210,3 +210,24 @@ def test_probe_mfma_argument_checks(lib):
     assert lib.sol_attn_probe_mfma(4, 0, FAKE, None) == 2
     assert lib.sol_attn_probe_mfma(4, 10, None, None) == 1
     assert lib.sol_attn_probe_mfma(4, 10, FAKE + 2, None) == 5
+
+
+@pytest.mark.parametrize("lang,std", [("c", "c99"), ("c++", "c++17")])
+def test_header_is_plain_c(lang, std, tmp_path):
+    """include/sol_attn.h is a C-ABI header: it compiles on its own as C99 and as C++17
+    (no torch or HIP types in the signatures), and a C program that includes it links
+    against the library and reads its version."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    inc = os.path.join(os.path.dirname(S.HEADER_PATH))
+    src = tmp_path / ("v.c" if lang == "c" else "v.cpp")
+    src.write_text('#include "sol_attn.h"\n#include <stdio.h>\n'
+                   'int main(void) { printf("%d\\n", sol_attn_version()); return 0; }\n')
+    exe = tmp_path / "v"
+    subprocess.run([cc, f"-std={std}", "-Wall", "-Werror", "-I", inc, str(src), "-o", str(exe),
+                    S.LIB_PATH, f"-Wl,-rpath,{os.path.dirname(S.LIB_PATH)}"], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0 and res.stdout.strip() == str(S.load_library().sol_attn_version())
