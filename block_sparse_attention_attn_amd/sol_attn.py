@@ -14,8 +14,11 @@ Calls (same names as the C ABI):
   sol_attn_window_blocks(n_blocks, topk)             -> int32 [n_blocks, topk] static window pattern
   sol_attn_check_block_idx(block_idx)                -> rows of an index list sol_attn_fwd does not accept
   sol_attn_cube_permute(x, grid, cube, inverse)      -> x with its tokens in cube-major (or frame-major) order
+  sol_attn_pool_cube(q, k, grid, cube)               -> box means of frame-major q, k (read in place)
+  sol_attn_fwd_cube(q, k, v, block_idx, grid, cube)  -> bf16 attention over boxes, frame-major in and out
   sparse_attention(q, k, v, block, topk)             -> the three calls in sequence
   cube_sparse_attention(q, k, v, grid, cube, topk)   -> the same with 3-D cube blocks
+  sol_attn_probe_mfma()                              -> sustained bf16 matrix-core TFLOP/s (diagnostic)
   sol_attn_quantize(x, fmt) / sol_attn_dequantize(codes, scales, fmt)
                                                      -> 8-bit exchange formats (INT8, FP8_E4M3)
 """
