@@ -15,6 +15,7 @@ the kernels of every timed step.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,8 +33,21 @@ PEAK_HBM_GBS = 8000.0
 # Memory-side traffic of one sol_attn_fwd launch on the headline workload (bytes):
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are
 # what the same counters read for a plain copy of known size in the same command).
-# Set to None whenever the kernel changes until it is measured again.
-FWD_TRAFFIC_BYTES = 47765202771   # fwd_bf16_kernel<false>, measured
+# The figure belongs to the kernel source whose SHA-256 prefix is stored beside it:
+# when csrc/fwd_bf16.hip differs, the traffic is reported as null until re-measured.
+FWD_TRAFFIC_BYTES = 47765202771
+FWD_TRAFFIC_SRC_SHA256 = "f4224e96746dcba0"   # the source as measured (its last change since was a comment)
+FWD_SRC = os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", "fwd_bf16.hip")
+
+
+def fwd_source_sha() -> str:
+    with open(FWD_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def fwd_traffic_bytes():
+    """The measured traffic if it was taken on the kernel source built here, else None."""
+    return FWD_TRAFFIC_BYTES if fwd_source_sha() == FWD_TRAFFIC_SRC_SHA256 else None
 
 
 def parse():
@@ -55,44 +69,75 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="after timing, run one plain device copy of Q (size known) to calibrate traffic counters")
-    p.add_argument("--cpu-heads", type=int, default=4,
-                   help="heads the CPU oracle runs for its baseline (about 10-30 s on 8-16 cores)")
+    p.add_argument("--cpu-workers", type=int, default=16,
+                   help="single-threaded oracle worker processes for the CPU baseline, one head each "
+                        "(at most the CPUs this process may use)")
     return p.parse_args()
 
 
-def cpu_baseline(wl, q, k, v, topk, n_heads, pattern="selected"):
-    """Time the float64 oracle as it stands -- pool, select and attend, every query
-    block (or, for the static window pattern, attend alone) -- on the first `n_heads`
-    (b, h) heads of the workload."""
+def _oracle_head(job):
+    """One (b, h) head of the oracle's whole path (runs in a single-threaded worker)."""
     import oracle
+    wl, q, k, v, topk, pattern = job
+    if pattern == "cube":
+        oracle.run_cube(q, k, v, wl.dtype, wl.grid, wl.cube, topk)
+    elif pattern == "window":
+        sel = oracle.window_selection(wl.n_blocks, topk)[None]
+        oracle.attend(oracle.widen(q, wl.dtype), oracle.widen(k, wl.dtype), oracle.widen(v, wl.dtype), sel,
+                      wl.block)
+    else:
+        oracle.run(q, k, v, wl.dtype, wl.block, topk)
+    return True
+
+
+def _single_thread_worker():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    qs = q.reshape(-1, wl.L, wl.d)[:n_heads]
-    ks = k.reshape(-1, wl.L, wl.d)[:n_heads]
-    vs = v.reshape(-1, wl.L, wl.d)[:n_heads]
-    t0 = time.perf_counter()
+        pass
+
+
+def cpu_baseline(wl, q, k, v, topk, max_workers, pattern="selected"):
+    """Time the float64 oracle as it stands -- pool, select and attend of every query
+    block (for the static window pattern: attend alone) -- on the first `workers` (b, h)
+    heads of the workload, one head per single-threaded worker process.  Runs before the
+    GPU is initialised (the workers are forked from a process that has not touched it)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    workers = max(1, min(max_workers, avail, wl.B * wl.H))
     if pattern == "quant":
         pattern = "selected"
+    qs, ks, vs = (x.reshape(-1, 1, wl.L, wl.d)[:workers] for x in (q, k, v))
+    jobs = [(wl, qs[i], ks[i], vs[i], topk, pattern) for i in range(workers)]
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork"),
+                                initializer=_single_thread_worker) as ex:
+        list(ex.map(lambda_ok, range(workers)))            # workers up before the clock starts
+        t0 = time.perf_counter()
+        list(ex.map(_oracle_head, jobs))
+        dt = time.perf_counter() - t0
     if pattern == "cube":
-        oracle.run_cube(qs, ks, vs, wl.dtype, wl.grid, wl.cube, topk)
         what = (f"whole path with {'x'.join(map(str, wl.cube))} cube blocks (pool, scores, top-{topk}, float64 "
                 f"attention of all {wl.n_blocks} query boxes)")
     elif pattern == "window":
-        sel = np.broadcast_to(oracle.window_selection(wl.n_blocks, topk), (n_heads, wl.n_blocks, topk))
-        oracle.attend(oracle.widen(qs, wl.dtype), oracle.widen(ks, wl.dtype), oracle.widen(vs, wl.dtype), sel,
-                      wl.block)
         what = f"float64 attention of all {wl.n_blocks} query blocks over the static window of {topk} blocks"
     else:
-        oracle.run(qs, ks, vs, wl.dtype, wl.block, topk)
-        what = (f"whole path (pool, scores, top-{topk}, float64 attention of all {wl.n_blocks} query blocks)")
-    dt = time.perf_counter() - t0
-    flops = 4.0 * n_heads * wl.L * (topk * wl.block) * wl.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"{n_heads} of {wl.B * wl.H} heads, {what}; TFLOP/s in the same effective-flop count"}
+        what = f"whole path (pool, scores, top-{topk}, float64 attention of all {wl.n_blocks} query blocks)"
+    flops = 4.0 * workers * wl.L * (topk * wl.block) * wl.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "seconds": round(dt, 3), "host_cpus_visible": int(avail),
+            "sample": f"{workers} of {wl.B * wl.H} heads, one head per single-threaded worker process, {what}; "
+                      f"TFLOP/s in the same effective-flop count"}
+
+
+def lambda_ok(_):
+    return True
 
 
 def main():
@@ -101,16 +146,19 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the sparse-attention path has no "
               f"multi-GPU mode", file=sys.stderr)
         sys.exit(2)
-    import torch
-    from block_sparse_attention_attn_amd import sol_attn as S
     from block_sparse_attention_attn_amd import workloads as W
 
-    S.load_library()
     wl = W.get(args.workload)
     topk = args.topk or wl.topk
     t_gen = time.perf_counter()
     q, k, v = W.make_qkv(wl)
     t_gen = time.perf_counter() - t_gen
+    # the CPU baseline runs first, in worker processes forked before anything touches the GPU
+    cpu_rec = None if args.no_cpu_baseline else cpu_baseline(wl, q, k, v, topk, args.cpu_workers, args.pattern)
+
+    import torch
+    from block_sparse_attention_attn_amd import sol_attn as S
+    S.load_library()
 
     def dev(x):
         x = np.ascontiguousarray(x)
@@ -337,8 +385,8 @@ def main():
             2.0 * wl.B * wl.H * nb * nb * wl.d / (t_sel * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": FWD_TRAFFIC_BYTES if (wl.name == "refine_1344x768" and topk == wl.topk
-                                                      and args.pattern == "selected") else None},
+                     "traffic": fwd_traffic_bytes() if (wl.name == "refine_1344x768" and topk == wl.topk
+                                                        and args.pattern == "selected") else None},
         **({"permute_gbs": round(4 * 2 * wl.B * wl.H * wl.L * row_bytes
                                  / ((t_phase["permute_in"] + t_phase["permute_out"]) * 1e-3) / 1e9, 1)}
            if reorder else {}),
@@ -346,8 +394,8 @@ def main():
         "timed_wall_s": round(wall, 3),
         "input_gen_s": round(t_gen, 2),
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_heads, args.pattern)
+    if cpu_rec is not None:
+        rec["cpu_baseline"] = cpu_rec
     print(json.dumps(rec), flush=True)
 
 

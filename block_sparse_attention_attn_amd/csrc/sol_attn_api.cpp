@@ -18,7 +18,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) {
+sol_attn_status_t fail(sol_attn_status_t code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -28,21 +28,21 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+sol_attn_status_t ok() {
   g_last_error.clear();
   return SOL_ATTN_OK;
 }
 
-int hip_status(hipError_t e, const char* what) {
+sol_attn_status_t hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(SOL_ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_common(int dtype, int B, int H, int L, int d, int block) {
+sol_attn_status_t check_common(sol_attn_dtype_t dtype, int B, int H, int L, int d, int block) {
   if (dtype != SOL_ATTN_BF16 && dtype != SOL_ATTN_FP32)
-    return fail(SOL_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    return fail(SOL_ATTN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (B < 0 || H < 0 || L < 0) return fail(SOL_ATTN_ERR_SHAPE, "negative size B=%d H=%d L=%d", B, H, L);
   if (d <= 0 || block <= 0) return fail(SOL_ATTN_ERR_SHAPE, "d=%d and block=%d must be positive", d, block);
   if ((long long)B * H > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "B*H too large");
@@ -53,9 +53,9 @@ int check_common(int dtype, int B, int H, int L, int d, int block) {
 
 extern "C" {
 
-int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, int d, int block,
-                  double* q_pooled, double* k_pooled, void* stream) {
-  int st = check_common(dtype, B, H, L, d, block);
+sol_attn_status_t sol_attn_pool(const void* q, const void* k, sol_attn_dtype_t dtype, int B, int H, int L, int d, int block,
+                                double* q_pooled, double* k_pooled, void* stream) {
+  sol_attn_status_t st = check_common(dtype, B, H, L, d, block);
   if (st != SOL_ATTN_OK) return st;
   const bool bf16 = dtype == SOL_ATTN_BF16;
   if (d > 512 || d % (bf16 ? 8 : 4) != 0)
@@ -73,8 +73,8 @@ int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, 
                     "pool launch");
 }
 
-int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,
-                    int topk, int32_t* block_idx, double* scores_or_null, void* stream) {
+sol_attn_status_t sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,
+                                  int topk, int32_t* block_idx, double* scores_or_null, void* stream) {
   if (B < 0 || H < 0 || n_blocks < 0) return fail(SOL_ATTN_ERR_SHAPE, "negative size");
   if (d <= 0) return fail(SOL_ATTN_ERR_SHAPE, "d=%d must be positive", d);
   if (d > 512) return fail(SOL_ATTN_ERR_UNSUPPORTED, "select needs d <= 512 (d=%d)", d);
@@ -93,10 +93,10 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
                     "select launch");
 }
 
-int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
-                 int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
-                 float softmax_scale, void* out, float* lse_or_null, void* stream) {
-  int st = check_common(dtype, B, H, L, d, block);
+sol_attn_status_t sol_attn_fwd(const void* q, const void* k, const void* v, sol_attn_dtype_t dtype, int B, int H, int L, int d,
+                               int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                               float softmax_scale, void* out, float* lse_or_null, void* stream) {
+  sol_attn_status_t st = check_common(dtype, B, H, L, d, block);
   if (st != SOL_ATTN_OK) return st;
   const bool bf16 = dtype == SOL_ATTN_BF16;
   if (bf16 && !(d == 128 && block == 128))
@@ -130,8 +130,8 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
                     "fwd fp32 launch");
 }
 
-int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
-                          int by, int bx, int inverse, void* stream) {
+sol_attn_status_t sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
+                                        int by, int bx, int inverse, void* stream) {
   if (B < 0 || H < 0 || T < 0 || h < 0 || w < 0)
     return fail(SOL_ATTN_ERR_SHAPE, "cube_permute: negative size B=%d H=%d T=%d h=%d w=%d", B, H, T, h, w);
   if (row_bytes <= 0 || row_bytes % 4 != 0)
@@ -157,7 +157,7 @@ int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h
 namespace {
 
 // The latent grid and box of the cube-block calls; on success *L is T*h*w.
-int check_cube(const char* call, int B, int H, int T, int h, int w, int bt, int by, int bx, long long* L) {
+sol_attn_status_t check_cube(const char* call, int B, int H, int T, int h, int w, int bt, int by, int bx, long long* L) {
   if (B < 0 || H < 0 || T < 0 || h < 0 || w < 0)
     return fail(SOL_ATTN_ERR_SHAPE, "%s: negative size B=%d H=%d T=%d h=%d w=%d", call, B, H, T, h, w);
   if (bt < 1 || by < 1 || bx < 1 || T % bt || h % by || w % bx)
@@ -170,10 +170,10 @@ int check_cube(const char* call, int B, int H, int T, int h, int w, int bt, int 
 
 }  // namespace
 
-int sol_attn_pool_cube(const void* q, const void* k, int dtype, int B, int H, int T, int h, int w, int d, int bt,
-                       int by, int bx, double* q_pooled, double* k_pooled, void* stream) {
+sol_attn_status_t sol_attn_pool_cube(const void* q, const void* k, sol_attn_dtype_t dtype, int B, int H, int T, int h, int w, int d, int bt,
+                                     int by, int bx, double* q_pooled, double* k_pooled, void* stream) {
   long long L = 0;
-  int st = check_cube("pool_cube", B, H, T, h, w, bt, by, bx, &L);
+  sol_attn_status_t st = check_cube("pool_cube", B, H, T, h, w, bt, by, bx, &L);
   if (st != SOL_ATTN_OK) return st;
   const long long V = (long long)bt * by * bx;
   if (V > 0x7fffffffLL) return fail(SOL_ATTN_ERR_SHAPE, "pool_cube: box of %lld tokens too large", V);
@@ -195,11 +195,11 @@ int sol_attn_pool_cube(const void* q, const void* k, int dtype, int B, int H, in
                     "pool_cube launch");
 }
 
-int sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H, int T, int h, int w, int bt, int by,
-                      int bx, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
-                      float softmax_scale, void* out, float* lse_or_null, void* stream) {
+sol_attn_status_t sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H, int T, int h, int w, int bt, int by,
+                                    int bx, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                                    float softmax_scale, void* out, float* lse_or_null, void* stream) {
   long long L = 0;
-  int st = check_cube("fwd_cube", B, H, T, h, w, bt, by, bx, &L);
+  sol_attn_status_t st = check_cube("fwd_cube", B, H, T, h, w, bt, by, bx, &L);
   if (st != SOL_ATTN_OK) return st;
   if ((long long)bt * by * bx != 128)
     return fail(SOL_ATTN_ERR_UNSUPPORTED, "fwd_cube needs boxes of 128 tokens (box %dx%dx%d)", bt, by, bx);
@@ -224,7 +224,7 @@ int sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H,
 
 namespace {
 
-int check_quant(const char* call, int B, int H, int L, int d, int format) {
+sol_attn_status_t check_quant(const char* call, int B, int H, int L, int d, int format) {
   if (B < 0 || H < 0 || L < 0) return fail(SOL_ATTN_ERR_SHAPE, "%s: negative size B=%d H=%d L=%d", call, B, H, L);
   if (d <= 0) return fail(SOL_ATTN_ERR_SHAPE, "%s: d=%d must be positive", call, d);
   if (format != SOL_ATTN_INT8 && format != SOL_ATTN_FP8_E4M3)
@@ -235,9 +235,9 @@ int check_quant(const char* call, int B, int H, int L, int d, int format) {
 
 }  // namespace
 
-int sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, void* codes, float* scales,
-                      void* stream) {
-  int st = check_quant("quantize", B, H, L, d, format);
+sol_attn_status_t sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, void* codes, float* scales,
+                                    void* stream) {
+  sol_attn_status_t st = check_quant("quantize", B, H, L, d, format);
   if (st != SOL_ATTN_OK) return st;
   const long long rows = (long long)B * H * L;
   if (rows == 0) return ok();
@@ -250,9 +250,9 @@ int sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, voi
                     "quantize launch");
 }
 
-int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
-                        void* stream) {
-  int st = check_quant("dequantize", B, H, L, d, format);
+sol_attn_status_t sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
+                                      void* stream) {
+  sol_attn_status_t st = check_quant("dequantize", B, H, L, d, format);
   if (st != SOL_ATTN_OK) return st;
   const long long rows = (long long)B * H * L;
   if (rows == 0) return ok();
@@ -265,8 +265,8 @@ int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, in
                     "dequantize launch");
 }
 
-int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_blocks, int topk, int32_t* bad_rows,
-                             void* stream) {
+sol_attn_status_t sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_blocks, int topk, int32_t* bad_rows,
+                                           void* stream) {
   if (B < 0 || H < 0 || n_blocks < 0 || topk < 0)
     return fail(SOL_ATTN_ERR_SHAPE, "check_block_idx: negative size B=%d H=%d n_blocks=%d topk=%d", B, H, n_blocks,
                 topk);
@@ -281,7 +281,7 @@ int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_block
                     "check_block_idx launch");
 }
 
-int sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream) {
+sol_attn_status_t sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream) {
   if (workgroups < 1 || iters < 1) return fail(SOL_ATTN_ERR_SHAPE, "probe_mfma: workgroups and iters must be >= 1");
   if (!sink) return fail(SOL_ATTN_ERR_NULL, "probe_mfma: NULL sink");
   if (!aligned(sink, 4)) return fail(SOL_ATTN_ERR_ALIGN, "probe_mfma: sink not 4-byte aligned");
@@ -289,7 +289,7 @@ int sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream) {
                     "probe_mfma launch");
 }
 
-int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
+sol_attn_status_t sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host) {
   if (block <= 0 || L < 0 || frame_tokens <= 0 || row_tokens <= 0 || row_tokens > frame_tokens)
     return fail(SOL_ATTN_ERR_SHAPE, "frame_order: bad geometry L=%d block=%d frame=%d row=%d", L, block,
                 frame_tokens, row_tokens);
@@ -308,7 +308,7 @@ int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int
   return ok();
 }
 
-int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host) {
+sol_attn_status_t sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host) {
   if (n_blocks < 0) return fail(SOL_ATTN_ERR_SHAPE, "window_blocks: n_blocks=%d < 0", n_blocks);
   if (n_blocks == 0) return ok();
   if (topk < 1 || topk > n_blocks)

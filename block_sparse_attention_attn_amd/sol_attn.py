@@ -190,7 +190,9 @@ def sol_attn_window_blocks(n_blocks: int, topk: int) -> torch.Tensor:
 
 def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor, block: int,
                  softmax_scale: Optional[float] = None, return_lse: bool = False,
-                 out: Optional[torch.Tensor] = None, qblock_order: Optional[torch.Tensor] = None):
+                 out: Optional[torch.Tensor] = None, qblock_order: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None):
+    """`out` / `lse` (optional): caller-provided outputs; passing `lse` implies return_lse."""
     lib = load_library()
     _check_qkv(q, k, v)
     B, H, L, d = q.shape
@@ -201,7 +203,15 @@ def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: t
         raise ValueError("block_idx leading dims must be [B,H,L/block]")
     if out is None:
         out = torch.empty_like(q)
-    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is not None:
+        if (tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32 or lse.device != q.device
+                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 [B,H,L] tensor on q's device")
+        return_lse = True
+    elif return_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     if qblock_order is not None:
         if (qblock_order.dtype != torch.int32 or qblock_order.device != q.device or
                 qblock_order.numel() != (-(-L // block) if block > 0 else 0) or not qblock_order.is_contiguous()):

@@ -60,7 +60,9 @@ extern "C" {
 
 typedef enum {
   SOL_ATTN_BF16 = 0,  /* bfloat16 inputs/outputs, float32 accumulation */
-  SOL_ATTN_FP32 = 1   /* float32 inputs/outputs, float32 arithmetic */
+  SOL_ATTN_FP32 = 1,  /* float32 inputs/outputs, float32 arithmetic */
+  SOL_ATTN_DTYPE_INT_RANGE_ = 0x7fffffff  /* not a dtype: makes any int a valid value of the type, so an
+                                             unknown code is rejected (SOL_ATTN_ERR_UNSUPPORTED), never UB */
 } sol_attn_dtype_t;
 
 typedef enum {
@@ -89,8 +91,8 @@ typedef enum {
  *               the division is IEEE-correctly rounded.
  * Supported: dtype BF16 with d % 8 == 0, or FP32 with d % 4 == 0; d <= 512; any block >= 1.
  */
-int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, int d, int block,
-                  double* q_pooled, double* k_pooled, void* stream);
+sol_attn_status_t sol_attn_pool(const void* q, const void* k, sol_attn_dtype_t dtype, int B, int H, int L, int d, int block,
+                                double* q_pooled, double* k_pooled, void* stream);
 
 /*
  * Top-k key-block selection per query block (the second half of the preparation).
@@ -102,8 +104,8 @@ int sol_attn_pool(const void* q, const void* k, int dtype, int B, int H, int L, 
  * Supported: 1 <= d <= 512, n_blocks <= 8192, 1 <= topk <= n_blocks.  -0.0 and +0.0 rank as equal.
  * Rows whose scores contain NaN get an unspecified (but in-range) selection.
  */
-int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,
-                    int topk, int32_t* block_idx, double* scores_or_null, void* stream);
+sol_attn_status_t sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H, int n_blocks, int d,
+                                  int topk, int32_t* block_idx, double* scores_or_null, void* stream);
 
 /*
  * Block-sparse exact softmax attention over the selected key blocks.
@@ -128,10 +130,22 @@ int sol_attn_select(const double* q_pooled, const double* k_pooled, int B, int H
  * Supported: BF16 with d == 128 and block == 128 (matrix-core path, float32 accumulation;
  * probabilities are rounded to bf16 before the P.V product), or FP32 with d in {64,128}
  * and 1 <= block <= 256.  16-byte alignment for q,k,v,out; 4-byte for lse and block_idx.
+ *
+ * Deliberate differences from the plain three-call interface (pool, select, fwd over
+ * Q/K/V [B,H,L,d] plus block size and k), each a strict extension:
+ *   - qblock_order_or_null is an extra argument; NULL gives the plain call.  It exists
+ *     because the launch order decides how many gathered K/V tiles come from cache, and
+ *     only the caller knows the latent grid that makes a good order.
+ *   - L need not be a multiple of block (a short last block, described above) instead of
+ *     being rejected with SOL_ATTN_ERR_SHAPE.
+ *   - FP32 accepts any block in [1, 256], not only 64 and 128.
+ *   - block_idx is not checked inside this call (no device error word); rows are clamped
+ *     into range so a bad list cannot fault, and sol_attn_check_block_idx validates a
+ *     list on the device when the caller wants it.
  */
-int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int L, int d,
-                 int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
-                 float softmax_scale, void* out, float* lse_or_null, void* stream);
+sol_attn_status_t sol_attn_fwd(const void* q, const void* k, const void* v, sol_attn_dtype_t dtype, int B, int H, int L, int d,
+                               int block, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                               float softmax_scale, void* out, float* lse_or_null, void* stream);
 
 /*
  * Device-side validation of a block index list (for lists not made by sol_attn_select,
@@ -144,8 +158,8 @@ int sol_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B, 
  * (or a NULL block_idx with rows to check), SOL_ATTN_ERR_ALIGN for pointers not 4-byte
  * aligned.  topk == 0 or no rows: bad_rows is set to 0.
  */
-int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_blocks, int topk, int32_t* bad_rows,
-                             void* stream);
+sol_attn_status_t sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_blocks, int topk, int32_t* bad_rows,
+                                           void* stream);
 
 /*
  * Host helper (no GPU work): a query-block schedule for frame-major video tokens.
@@ -158,7 +172,7 @@ int sol_attn_check_block_idx(const int32_t* block_idx, int B, int H, int n_block
  * Returns SOL_ATTN_ERR_SHAPE unless block > 0, L >= 0, frame_tokens > 0 and
  * 0 < row_tokens <= frame_tokens.
  */
-int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host);
+sol_attn_status_t sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int32_t* order_host);
 
 /*
  * Host helper (no GPU work): a static block-sparse pattern for sol_attn_fwd, the
@@ -174,7 +188,7 @@ int sol_attn_frame_order(int L, int block, int frame_tokens, int row_tokens, int
  * Returns SOL_ATTN_ERR_SHAPE if n_blocks < 0, SOL_ATTN_ERR_K unless 1 <= topk <= n_blocks
  * (when n_blocks > 0), SOL_ATTN_ERR_NULL for a NULL output with n_blocks > 0.
  */
-int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
+sol_attn_status_t sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
 
 /*
  * Token reordering for 3-D cube blocks (device copy).  The tokens of a clip form a
@@ -198,8 +212,8 @@ int sol_attn_window_blocks(int n_blocks, int topk, int32_t* idx_host);
  * Returns SOL_ATTN_ERR_SHAPE for negative sizes, row_bytes not a positive multiple of 4,
  * a box that does not divide the grid (no partial boxes), inverse not 0/1, or B*H > 65535.
  */
-int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
-                          int by, int bx, int inverse, void* stream);
+sol_attn_status_t sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h, int w, int row_bytes, int bt,
+                                        int by, int bx, int inverse, void* stream);
 
 /*
  * Cube blocks read in place: sol_attn_pool with the blocks replaced by the bt x by x bx
@@ -211,8 +225,8 @@ int sol_attn_cube_permute(const void* src, void* dst, int B, int H, int T, int h
  * Errors: as sol_attn_cube_permute for the grid and box (SOL_ATTN_ERR_SHAPE), then as
  * sol_attn_pool for dtype, d, B*H, NULL and alignment.
  */
-int sol_attn_pool_cube(const void* q, const void* k, int dtype, int B, int H, int T, int h, int w, int d, int bt,
-                       int by, int bx, double* q_pooled, double* k_pooled, void* stream);
+sol_attn_status_t sol_attn_pool_cube(const void* q, const void* k, sol_attn_dtype_t dtype, int B, int H, int T, int h, int w, int d, int bt,
+                                     int by, int bx, double* q_pooled, double* k_pooled, void* stream);
 
 /*
  * Cube blocks read in place: the bf16 sol_attn_fwd (d = 128) with query and key block
@@ -226,9 +240,9 @@ int sol_attn_pool_cube(const void* q, const void* k, int dtype, int B, int H, in
  * SOL_ATTN_ERR_UNSUPPORTED for a box of other than 128 tokens or a head of 2^31 bytes
  * or more; then as sol_attn_fwd.
  */
-int sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H, int T, int h, int w, int bt, int by,
-                      int bx, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
-                      float softmax_scale, void* out, float* lse_or_null, void* stream);
+sol_attn_status_t sol_attn_fwd_cube(const void* q, const void* k, const void* v, int B, int H, int T, int h, int w, int bt, int by,
+                                    int bx, int topk, const int32_t* block_idx, const int32_t* qblock_order_or_null,
+                                    float softmax_scale, void* out, float* lse_or_null, void* stream);
 
 /*
  * 8-bit exchange formats.  Between GPUs the Sol-H3 runtime sends Q, K and V as INT8 and
@@ -252,16 +266,16 @@ typedef enum { SOL_ATTN_INT8 = 0, SOL_ATTN_FP8_E4M3 = 1 } sol_attn_qformat_t;
  *   scales  [B,H,L] float32 output (one per row); 4-byte aligned.
  * Supported: d % 8 == 0, d <= 512.  Inputs must be finite.
  */
-int sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, void* codes, float* scales,
-                      void* stream);
+sol_attn_status_t sol_attn_quantize(const void* x, int B, int H, int L, int d, int format, void* codes, float* scales,
+                                    void* stream);
 
 /*
  * Decode rows written by sol_attn_quantize (same format) to bf16.
  *   codes [B,H,L,d] bytes (8-byte aligned), scales [B,H,L] float32 (4-byte aligned),
  *   out   [B,H,L,d] bf16 output (16-byte aligned).  Same support as sol_attn_quantize.
  */
-int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
-                        void* stream);
+sol_attn_status_t sol_attn_dequantize(const void* codes, const float* scales, int B, int H, int L, int d, int format, void* out,
+                                      void* stream);
 
 /*
  * Diagnostic (not part of the method): launches `workgroups` workgroups of 4 waves, each
@@ -272,7 +286,7 @@ int sol_attn_dequantize(const void* codes, const float* scales, int B, int H, in
  *         the products from being optimised away); 4-byte aligned.
  * Returns SOL_ATTN_ERR_SHAPE unless workgroups, iters >= 1; SOL_ATTN_ERR_NULL for a NULL sink.
  */
-int sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream);
+sol_attn_status_t sol_attn_probe_mfma(int workgroups, int iters, float* sink, void* stream);
 
 /* Human-readable description of the last failure on the calling thread ("" if none). */
 const char* sol_attn_last_error(void);

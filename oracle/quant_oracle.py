@@ -19,12 +19,17 @@ The reading implemented
   subnormals, largest finite 448, no infinities, S.1111.111 = NaN);
   stored scale amax / 448; code = x * (448 / amax) rounded to nearest-even E4M3,
   saturated to +-448.
-* The page fixes no rounding order; the value coded is x times the reciprocal scale,
-  taken once per row (one division per row rather than per value).
+* The page fixes no rounding order.  The reading taken is the published absmax
+  scheme of LLM.int8() (Dettmers et al., 2022, section on absmax quantization): a
+  per-row scaling constant qmax/amax, and code = round(constant * x).  So the value
+  coded is fl32(x * fl32(qmax/amax)); the stored scale amax/qmax is what the receiver
+  multiplies by.  Dividing each value by the stored scale is the other possible order
+  and gives different codes on ordinary rows; tests/test_oracle_exact_pins.py pins
+  this reading against exact rational arithmetic and shows the two orders differ.
 * A row of zeros gets scale 0 and all-zero codes.
 * Decoding: value = code * scale, rounded to bf16 (nearest-even).
-* Every quantity that decides a code is float32, computed with IEEE-rounded float32
-  division and multiplication, as the kernels do.
+* Every quantity that decides a code is float32 with IEEE-rounded float32 division
+  and multiplication (the exchanged scale is a float32).
 
 Library primitives used as single steps: numpy float32 arithmetic, rint, abs/max.
 """

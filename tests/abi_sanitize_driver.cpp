@@ -12,22 +12,22 @@ int main() {
   void* M = reinterpret_cast<void*>(0x10002);
   int32_t* I = reinterpret_cast<int32_t*>(0x10000);
   double* D = reinterpret_cast<double*>(0x10000);
-  EXPECT(sol_attn_fwd(F, F, F, 7, 1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 4);
-  EXPECT(sol_attn_fwd(F, F, F, 0, -1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 2);
-  EXPECT(sol_attn_fwd(F, F, F, 0, 1, 1, 256, 128, 128, 3, I, nullptr, 0.f, F, nullptr, nullptr), 3);
-  EXPECT(sol_attn_fwd(nullptr, F, F, 0, 1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 1);
-  EXPECT(sol_attn_fwd(F, F, M, 0, 1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 5);
-  EXPECT(sol_attn_fwd(F, F, F, 0, 1, 1, 9000000, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 4);
-  EXPECT(sol_attn_fwd(F, F, F, 0, 0, 1, 256, 128, 128, 99, I, nullptr, 0.f, F, nullptr, nullptr), 0);
-  EXPECT(sol_attn_pool(F, F, 3, 1, 1, 256, 128, 128, D, D, nullptr), 4);
-  EXPECT(sol_attn_pool(F, F, 0, 1, 1, 256, 12, 128, D, D, nullptr), 4);
-  EXPECT(sol_attn_pool(F, nullptr, 0, 1, 1, 256, 128, 128, D, D, nullptr), 1);
+  EXPECT(sol_attn_fwd(F, F, F, (sol_attn_dtype_t)7, 1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 4);
+  EXPECT(sol_attn_fwd(F, F, F, (sol_attn_dtype_t)0, -1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 2);
+  EXPECT(sol_attn_fwd(F, F, F, (sol_attn_dtype_t)0, 1, 1, 256, 128, 128, 3, I, nullptr, 0.f, F, nullptr, nullptr), 3);
+  EXPECT(sol_attn_fwd(nullptr, F, F, (sol_attn_dtype_t)0, 1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 1);
+  EXPECT(sol_attn_fwd(F, F, M, (sol_attn_dtype_t)0, 1, 1, 256, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 5);
+  EXPECT(sol_attn_fwd(F, F, F, (sol_attn_dtype_t)0, 1, 1, 9000000, 128, 128, 1, I, nullptr, 0.f, F, nullptr, nullptr), 4);
+  EXPECT(sol_attn_fwd(F, F, F, (sol_attn_dtype_t)0, 0, 1, 256, 128, 128, 99, I, nullptr, 0.f, F, nullptr, nullptr), 0);
+  EXPECT(sol_attn_pool(F, F, (sol_attn_dtype_t)3, 1, 1, 256, 128, 128, D, D, nullptr), 4);
+  EXPECT(sol_attn_pool(F, F, (sol_attn_dtype_t)0, 1, 1, 256, 12, 128, D, D, nullptr), 4);
+  EXPECT(sol_attn_pool(F, nullptr, (sol_attn_dtype_t)0, 1, 1, 256, 128, 128, D, D, nullptr), 1);
   EXPECT(sol_attn_select(D, D, 1, 1, 8, 128, 0, I, nullptr, nullptr), 3);
   EXPECT(sol_attn_select(D, D, 1, 1, 8193, 128, 1, I, nullptr, nullptr), 4);
   EXPECT(sol_attn_select(D, D, 1, 1, 0, 128, 0, I, nullptr, nullptr), 0);
   EXPECT(sol_attn_cube_permute(F, F, 1, 1, 4, 16, 16, 256, 3, 8, 8, 0, nullptr), 2);
   EXPECT(sol_attn_cube_permute(F, F, 1, 1, 4, 16, 16, 6, 2, 8, 8, 0, nullptr), 2);
-  EXPECT(sol_attn_pool_cube(F, F, 0, 1, 1, 4, 16, 16, 128, 2, 3, 8, D, D, nullptr), 2);
+  EXPECT(sol_attn_pool_cube(F, F, (sol_attn_dtype_t)0, 1, 1, 4, 16, 16, 128, 2, 3, 8, D, D, nullptr), 2);
   EXPECT(sol_attn_fwd_cube(F, F, F, 1, 1, 4, 16, 16, 1, 4, 4, 2, I, nullptr, 0.f, F, nullptr, nullptr), 4);
   EXPECT(sol_attn_fwd_cube(F, F, F, 1, 1, 1024, 256, 256, 2, 8, 8, 2, I, nullptr, 0.f, F, nullptr, nullptr), 4);
   EXPECT(sol_attn_quantize(F, 1, 1, 8, 128, 7, F, reinterpret_cast<float*>(F), nullptr), 4);

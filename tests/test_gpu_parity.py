@@ -232,20 +232,76 @@ def test_fwd_deterministic(S):
 FULL = ["draft_896x512", "refine_1344x768", "clip10s_1344x768", "refine_2k"]
 
 
+def sample_blocks(nb, order, rng, extra=1):
+    """Query blocks checked in every head: the first and last block, the two blocks on
+    either side of the first boundary between XCD work ranges in the launch schedule
+    (position per_xcd - 1 and per_xcd of `order`), and `extra` seeded random ones."""
+    per_xcd = -(-nb // 8)
+    picks = {0, nb - 1}
+    if per_xcd < nb:
+        picks |= {int(order[per_xcd - 1]), int(order[per_xcd])}
+    picks |= {int(i) for i in rng.choice(nb, extra, replace=False)}
+    return sorted(picks)
+
+
+def sampled_attention(Qd, Kd, Vd, sel, block, picks_per_head):
+    """Oracle O and lse of the given query blocks of every head (a thread pool over
+    blocks; numpy releases the GIL in matmul and exp).  Returns {(bh, i): (O_i, lse_i)}."""
+    BH, L, d = Qd.shape
+    jobs = [(bh, i) for bh in range(BH) for i in picks_per_head[bh]]
+
+    def one(job):
+        bh, i = job
+        s = oracle.block_rows(i, L, block)
+        return job, oracle.attend_block(Qd[bh, s], Kd[bh], Vd[bh], sel[bh, i], block, 1.0 / math.sqrt(d))
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        return dict(ex.map(one, jobs))
+
+
+def check_sampled(out, lse, ref, L, block, what):
+    o = out.view(-1, L, out.shape[-1])
+    ls = lse.view(-1, L)
+    errs, lerrs = [], []
+    for (bh, i), (Oi, lsei) in ref.items():
+        s = oracle.block_rows(i, L, block)
+        errs.append(np.abs(host_f64(o[bh, s]) - Oi))
+        lerrs.append(np.abs(ls[bh, s].double().cpu().numpy() - lsei))
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
+    log(f"{what}: {len(ref)} query blocks, max|err| {err.max():.3e} mean|err| {err.mean():.3e} "
+        f"max|lse err| {lerr.max():.3e}")
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (what, err.max(), err.mean())
+    assert lerr.max() <= 1e-3, (what, lerr.max())
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(S, name):
+    """Full-size workload in the launch configuration the benchmark times: pooled means
+    and every selected index bit-exact; every output row written; O and lse of four or
+    more query blocks in every head against the oracle; a second launch bit-identical
+    to the first (the kernel's waits and barriers leave no race)."""
     wl = W.get(name)
     log(f"full {name}: generating")
     q, k, v = W.make_qkv(wl)
     Q, K, V = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
     log(f"full {name}: gpu pool/select/fwd")
-    order = S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w).cuda()
+    order = S.sol_attn_frame_order(wl.L, wl.block, wl.lat_h * wl.lat_w, wl.lat_w)
+    order_d = order.cuda()
     qp, kp = S.sol_attn_pool(Q, K, wl.block)
     idx = S.sol_attn_select(qp, kp, wl.topk)
     out = torch.full_like(Q, float("nan"))
-    S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out, qblock_order=order)
+    lse = torch.full(Q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out, lse=lse, qblock_order=order_d)
     torch.cuda.synchronize()
+    log(f"full {name}: second launch (race check)")
+    out2 = torch.full_like(Q, float("nan"))
+    lse2 = torch.full_like(lse, float("nan"))
+    S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out2, lse=lse2, qblock_order=order_d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    del out2, lse2
     log(f"full {name}: oracle pool/select")
     Qd = oracle.widen(q, "bf16")
     qbar = oracle.pool(Qd, wl.block)
@@ -257,33 +313,29 @@ def test_full_size_workload(S, name):
     got = idx.cpu().numpy()
     assert np.array_equal(got, want)
     # every output row written, finite
-    assert not torch.isnan(out).any().item()
-    # sampled query blocks against the oracle
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
     log(f"full {name}: sampled attention")
     Vd = oracle.widen(v, "bf16")
+    BH, nb = wl.B * wl.H, wl.n_blocks
+    Qf, Kf, Vf = (x.reshape(BH, wl.L, wl.d) for x in (Qd, Kd, Vd))
     rng = np.random.default_rng(wl.seed)
-    o = out.view(wl.B * wl.H, wl.L, wl.d)
-    errs = []
-    for bh in rng.choice(wl.B * wl.H, 4, replace=False):
-        for i in list(rng.choice(wl.n_blocks, 2, replace=False)) + [wl.n_blocks - 1]:
-            s = slice(i * wl.block, (i + 1) * wl.block)
-            Oi, _ = oracle.attend_block(Qd.reshape(-1, wl.L, wl.d)[bh, s], Kd.reshape(-1, wl.L, wl.d)[bh],
-                                        Vd.reshape(-1, wl.L, wl.d)[bh], want.reshape(-1, wl.n_blocks, wl.topk)[bh, i],
-                                        wl.block, 1.0 / math.sqrt(wl.d))
-            errs.append(np.abs(host_f64(o[bh, s]) - Oi))
-    err = np.concatenate(errs)
-    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+    picks = [sample_blocks(nb, order, rng) for _ in range(BH)]
+    ref = sampled_attention(Qf, Kf, Vf, want.reshape(BH, nb, wl.topk), wl.block, picks)
+    check_sampled(out, lse, ref, wl.L, wl.block, f"full {name}")
     if name == "refine_2k":
-        # the dense (k = all blocks) run
+        # the dense (k = all blocks) run, into freshly NaN-filled outputs
         log("full refine_2k: dense k=1152")
-        kd = wl.n_blocks
+        kd = nb
         idx_d = S.sol_attn_select(qp, kp, kd)
-        assert torch.equal(idx_d[0, 0, 0].cpu(), torch.arange(kd, dtype=torch.int32))
-        S.sol_attn_fwd(Q, K, V, idx_d, wl.block, out=out, qblock_order=order)
+        assert torch.equal(idx_d.cpu(), torch.arange(kd, dtype=torch.int32).expand(wl.B, wl.H, kd, kd))
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        S.sol_attn_fwd(Q, K, V, idx_d, wl.block, out=out, lse=lse, qblock_order=order_d)
         torch.cuda.synchronize()
-        bh, i = 5, 17
-        s = slice(i * wl.block, (i + 1) * wl.block)
-        Oi, _ = oracle.attend_block(Qd.reshape(-1, wl.L, wl.d)[bh, s], Kd.reshape(-1, wl.L, wl.d)[bh],
-                                    Vd.reshape(-1, wl.L, wl.d)[bh], np.arange(kd), wl.block, 1.0 / math.sqrt(wl.d))
-        e = np.abs(host_f64(o[bh, s]) - Oi)
-        assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN, (e.max(), e.mean())
+        assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
+        del idx_d
+        dense = np.broadcast_to(np.arange(kd, dtype=np.int32), (BH, nb, kd))
+        rng = np.random.default_rng(44)
+        picks = [sample_blocks(nb, order, rng, extra=0) for _ in range(BH)]
+        ref = sampled_attention(Qf, Kf, Vf, dense, wl.block, picks)
+        check_sampled(out, lse, ref, wl.L, wl.block, "full refine_2k dense")

@@ -116,7 +116,10 @@ def test_ragged_bf16_many_blocks(S):
 @pytest.mark.timeout(900)
 def test_ragged_full_size(S):
     """The 1344x768 workload cut to 64,475 tokens (503 full blocks and one of 91): pooled
-    means and selections in full, attention on sampled blocks including the short one."""
+    means and every head's selection in full; O and lse of the short block and two
+    seeded blocks in every head, each against the oracle's own selection."""
+    import concurrent.futures as cf
+    import os
     wl = W.get("refine_1344x768")
     q, k, v = (x[..., :wl.L - 37, :] for x in W.make_qkv(wl))
     L = wl.L - 37
@@ -126,26 +129,34 @@ def test_ragged_full_size(S):
     qp, kp = S.sol_attn_pool(Q, K, wl.block)
     idx = S.sol_attn_select(qp, kp, wl.topk)
     out = torch.full_like(Q, float("nan"))
-    S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out, qblock_order=order)
+    _, lse = S.sol_attn_fwd(Q, K, V, idx, wl.block, out=out, qblock_order=order, return_lse=True)
     torch.cuda.synchronize()
     Qd, Kd, Vd = (oracle.widen(x, "bf16") for x in (q, k, v))
     qbar, kbar = oracle.pool(Qd, wl.block), oracle.pool(Kd, wl.block)
     assert np.array_equal(qp.cpu().numpy(), qbar) and np.array_equal(kp.cpu().numpy(), kbar)
-    B, H = wl.B, wl.H
-    got = idx.cpu().numpy()
-    for bh in range(0, B * H, 5):                         # selections: every 5th head in full
-        want = oracle.select(qbar.reshape(-1, nb, wl.d)[bh], kbar.reshape(-1, nb, wl.d)[bh], wl.topk)
-        assert np.array_equal(got.reshape(-1, nb, wl.topk)[bh], want)
+    BH = wl.B * wl.H
+    qf, kf = qbar.reshape(BH, nb, wl.d), kbar.reshape(BH, nb, wl.d)
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        want = np.stack(list(ex.map(lambda bh: oracle.select(qf[bh], kf[bh], wl.topk), range(BH))))
+    assert np.array_equal(idx.cpu().numpy().reshape(BH, nb, wl.topk), want)
     assert not torch.isnan(out).any().item()
-    o = out.view(-1, L, wl.d)
+    o, ls = out.view(BH, L, wl.d), lse.view(BH, L)
+    Qf, Kf, Vf = (x.reshape(BH, L, wl.d) for x in (Qd, Kd, Vd))
     rng = np.random.default_rng(1)
-    errs = []
-    for bh in rng.choice(B * H, 3, replace=False):
-        for i in [nb - 1] + list(rng.choice(nb - 1, 2, replace=False)):
-            s = oracle.block_rows(i, L, wl.block)
-            Oi, _ = oracle.attend_block(Qd.reshape(-1, L, wl.d)[bh, s], Kd.reshape(-1, L, wl.d)[bh],
-                                        Vd.reshape(-1, L, wl.d)[bh], got.reshape(-1, nb, wl.topk)[bh, i],
-                                        wl.block, 1.0 / math.sqrt(wl.d))
-            errs.append(np.abs(o[bh, s].float().double().cpu().numpy() - Oi))
-    err = np.concatenate(errs)
+    jobs = [(bh, i) for bh in range(BH) for i in [nb - 1] + list(rng.choice(nb - 1, 2, replace=False))]
+
+    def one(job):
+        bh, i = job
+        s = oracle.block_rows(i, L, wl.block)
+        return job, oracle.attend_block(Qf[bh, s], Kf[bh], Vf[bh], want[bh, i], wl.block, 1.0 / math.sqrt(wl.d))
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        ref = dict(ex.map(one, jobs))
+    errs, lerrs = [], []
+    for (bh, i), (Oi, lsei) in ref.items():
+        s = oracle.block_rows(i, L, wl.block)
+        errs.append(np.abs(o[bh, s].float().double().cpu().numpy() - Oi))
+        lerrs.append(np.abs(ls[bh, s].double().cpu().numpy() - lsei))
+    err, lerr = np.concatenate(errs), np.concatenate(lerrs)
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+    assert lerr.max() <= 1e-3, lerr.max()
