@@ -16,11 +16,13 @@
 //   S^T = K_j Q^T      16 MFMA 32x32x16: A = K rows from LDS (16-byte reads),
 //                      B = Q^T held in registers for the whole unit.  Computing
 //                      S transposed puts the keys of one query in the registers
-//                      of one lane pair (l, l^32), so the row max is an
-//                      in-register reduction plus one cross-half exchange.
-//   online softmax     in the log2 domain: t = s*scale*log2(e), m = running max,
-//                      p = 2^(t-m) (v_exp_f32), l += sum p, O *= 2^(m_old-m)
-//                      (skipped when no running max of the wave moved).
+//                      of one lane pair (l, l^32).
+//   softmax            in the log2 domain against the running max m of the wave's
+//                      key half: p = 2^(s*scale*log2(e) - m) (v_exp_f32), l += sum p.
+//                      The max is not recomputed per tile: the common factor 2^-m
+//                      cancels in O/l, so only a weight sum above 2^15 (a score that
+//                      rose far above m, or the first tile) makes the wave find the
+//                      row max, raise m and rescale O and l.
 //   O^T += V_j^T P^T   16 MFMA 32x32x16: the S^T accumulator layout already is
 //                      the B-operand layout of P^T (after bf16 rounding) for a
 //                      fixed permutation of the 16 keys of each k-step; the A
@@ -28,24 +30,35 @@
 //                      16-lane transpose delivers 4 consecutive keys of one
 //                      column per lane, in the same key permutation.
 //
-// Pipelining: S for tile t+1 is computed in the same iteration as the softmax and
-// PV of tile t, so K_j is read one iteration before V_j.  LDS holds three K tiles
-// and two V tiles (5 x 32 KiB, the whole 160 KiB): K_j in K buffer j%3, V_j in V
-// buffer j%2.  Iteration t refills the V buffer of V_{t-1} with V_{t+1} (issued after
-// the softmax) and the K buffer of K_t with K_{t+3} (one quarter of it in each k-step
-// of the PV products), so a K copy has about two iterations to land and a V copy
-// about half of one.  The barrier opening an iteration waits (s_waitcnt vmcnt) only
-// for this wave's copies the iteration reads, leaving the youngest K copy in flight;
-// copies spread through the iteration instead of issued in one burst at its start
-// run 5-7 % faster at the 1344x768 size (they slow the LDS reads of the products
-// less).  The byte offsets of a step's copies are computed during the previous
-// step's products (scalar work off the top of the step: 0.5 %).  The iterations are
-// unrolled six at a time (periods 3 and 2), so every buffer is a compile-time choice
-// and the compiler adds no waits of its own.  Operand reads run ahead of the
-// products: K four products ahead (the two 32-key S accumulators alternate), V three
-// (two transposed reads each).  The two key-half waves that share a SIMD run the S
-// product and the softmax in opposite order, so one wave's softmax (VALU, exp)
-// overlaps the other's matrix-core work.
+// Two waves share each SIMD: the two key halves of the same 32 queries.  Each step
+// (one tile) has two halves; in each, one wave of the pair runs its matrix phase --
+// S_{t+1} and O += V_t^T P_t^T, 32 products, at raised issue priority -- while the
+// other runs its softmax (the P it accumulates next); the roles swap in the second
+// half.  Key half 0 takes the matrix phase first, key half 1 second; the loop is
+// compiled once per key half so each wave runs straight-line code for its role.
+// Without this the older wave wins issue arbitration, runs ahead, and every step
+// ends with one wave alone on the SIMD (measured: the younger waves' steps set the
+// pace while the older ones idled a third of the time at the barrier).
+//
+// Copies: LDS holds three K tiles and two V tiles (5 x 32 KiB, the whole 160 KiB):
+// K_j in K buffer j%3 (read for S_j in step j-1), V_j in V buffer j%2 (read in step
+// j).  Step t refills V(t-1)'s buffer with V(t+1) and K(t)'s with K(t+3); each wave
+// issues its share of both from its softmax phase (V before the weights, K after),
+// so the matrix-phase wave only reads LDS.  The wait opening a step (vmcnt <= 4)
+// leaves only this wave's K(t+3) copies in flight, and the barrier after it makes
+// every wave's copies visible and frees the two buffers.  A step's block indices are
+// scalar loads issued before that wait, which drains the scalar/LDS counter anyway:
+// loaded later, their wait would also drain the operand reads running ahead of the
+// products.  Past the end of the list the last tile is copied again into the free
+// buffer (never read), keeping the copies per step fixed; each tile gets its own
+// buffer resource, whose range makes rows past the end of a short last block read as
+// zero.  The iterations are unrolled six at a time (periods 3 and 2), so every
+// buffer is a compile-time choice and the compiler adds no waits of its own.
+//
+// Where the time goes (1344x768 workload, per step and CU): 128 KiB of K operand
+// reads, 128 KiB of transposed V reads and 64 KiB of copies written land on an LDS
+// that moves 128 B per clock for 16-byte reads and 78-120 B per clock for transposed
+// reads: about 2900 clocks, against 2048 clocks of matrix-core work.
 //
 // LDS layout of a 128x128 bf16 tile: row r = 256 bytes = 16 chunks of 16 bytes;
 // logical chunk c lives at physical chunk c ^ swz(r), swz(r) = 4*(r%4) + (r/4)%4.
@@ -65,6 +78,8 @@
 // which leaves the LDS tile exactly as for 128 consecutive tokens; Q rows, O rows and
 // lse entries likewise sit at their frame-major positions.  No reordered copy of Q, K,
 // V or O is made.
+#include <type_traits>
+
 #include "launchers.h"
 
 namespace sol_attn {
@@ -86,6 +101,10 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+// how many products ahead of the matrix core the K and transposed V operand reads run
+// (deeper is slower: the reads then queue on the LDS, which is the busier unit)
+constexpr int kKAhead = 4;
+constexpr int kVAhead = 3;
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
@@ -111,10 +130,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // 4s + l/16, so it fetches the logical chunk that the swizzle places there; the
 // 16 lanes of a row still read that row's 256 contiguous bytes.  Wave w copies
 // segments w, w+8, w+16, w+24.  Completion is awaited by the next barrier.
-// Buffer resource of one head's K or V (raw, byte-addressed, range-checked: rows past
-// the end of the head -- the missing rows of a short last block -- read as zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const unsigned char* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0, bytes, 0x00020000);
+//
+// Each tile gets its own buffer resource whose base is the tile's first token and whose
+// range is the bytes the tile may read: rows past the end of the head (the missing rows
+// of a short last block) are outside it and read as zero.  The per-lane byte offsets
+// inside the tile are loop invariants, so a copy costs no vector arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned char* head, int off, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(head) + off, (short)0, bytes, 0x00020000);
 }
 
 // First token of key/query block j, and offset from it of the block's row r: blocks of
@@ -128,27 +150,19 @@ __device__ __forceinline__ int row_token_offset(const BoxGeom& g, int r) {
   return kCube ? g.row_offset(r) : r;
 }
 
-// Copy one tile (segments wave, wave+8, wave+16, wave+24 of 4 rows each) whose first
-// token starts at byte `off`; rowb[i] = byte offset of this lane's row of segment i.
-__device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off,
-                                         const int (&rowb)[4], int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int seg = wave + 8 * i;
-    const int row = 4 * seg + (lane >> 4);
-    const int c = (lane & 15) ^ swz(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16,
-                                             off + rowb[i] + c * 16, 0, 0, 0);
-  }
+// Copy segment i (of wave, wave+8, wave+16, wave+24) of a tile; laneoff[i] = byte offset,
+// from the tile's first token, of the 16 bytes this lane fetches for that segment.
+__device__ __forceinline__ void tile_dma_seg(unsigned char* lds, __amdgpu_buffer_rsrc_t r, const int (&laneoff)[4],
+                                             int wave, int i) {
+  const int seg = wave + 8 * i;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16,
+                                           laneoff[i], 0, 0, 0);
 }
 
-__device__ __forceinline__ void tile_dma_seg(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int off,
-                                             const int (&rowb)[4], int wave, int lane, int i) {
-  const int seg = wave + 8 * i;
-  const int row = 4 * seg + (lane >> 4);
-  const int c = (lane & 15) ^ swz(row);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + seg * 1024), 16,
-                                           off + rowb[i] + c * 16, 0, 0, 0);
+__device__ __forceinline__ void tile_dma(unsigned char* lds, __amdgpu_buffer_rsrc_t r, const int (&laneoff)[4],
+                                         int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tile_dma_seg(lds, r, laneoff, wave, i);
 }
 
 // Scores of keys past the end of the sequence (a short last key block) -> -inf.
@@ -160,6 +174,31 @@ __device__ __forceinline__ void mask_missing_keys(f32x16 (&s)[2], int key0, int 
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[mb][r] = 32 * mb + 8 * (r >> 2) + (r & 3) >= lim ? -INFINITY : s[mb][r];
+}
+
+// Weights p = 2^(s*scale_log2 - m) of this lane's 32 scores, rounded to bf16 into the P^T
+// operand layout (pb[k-step][dword]); returns this lane's float32 sum of the weights.
+// Score register r of s[mb] is key 32mb + 8(r/4) + 4h + r%4: k-step 2mb + r/8 takes
+// registers 8(r/8)..+7, dword 2((r/4)%2) + (r%4)/2 of it holds the pair (r, r+1).
+__device__ __forceinline__ float softmax_weights(const f32x16 (&s)[2], float scale_log2, float m,
+                                                 uint32_t (&pb)[4][4]) {
+  float acc0 = 0.f, acc1 = 0.f;   // two chains of additions
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mb][r], scale_log2, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][r + 1], scale_log2, -m));
+      pb[2 * mb + (r >> 3)][((r >> 2) & 1) * 2 + ((r & 3) >> 1)] = pack_bf16x2(p0, p1);
+      if (r & 2) acc1 += p0 + p1; else acc0 += p0 + p1;
+    }
+  // the packed weights are formed here, not next to the products that read them: 16
+  // registers instead of 32 live until then, and no conversions in the matrix phase
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) asm volatile("" : "+v"(pb[ks][dw]));
+  return acc0 + acc1;
 }
 
 // S^T (64 keys of this wave's half x 32 queries) = K_half . Q^T.
@@ -177,14 +216,14 @@ __device__ __forceinline__ void compute_st(f32x16 (&s)[2], const unsigned char* 
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
     }
   }
-  // operand reads run four products ahead of the matrix core (deeper costs registers)
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+  // operand reads run kKAhead products ahead of the matrix core (deeper costs registers)
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kKAhead, 0);
 #pragma unroll
-  for (int i = 0; i < 12; ++i) {
+  for (int i = 0; i < 16 - kKAhead; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kKAhead, 0);
 }
 
 template <bool kCube>
@@ -224,19 +263,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int key0 = 64 * kh;
 
   const size_t head_off = (size_t)bh * L * kD * 2;    // bytes
-  const __amdgpu_buffer_rsrc_t k_rsrc = head_rsrc(k + head_off, L * kD * 2);
-  const __amdgpu_buffer_rsrc_t v_rsrc = head_rsrc(v + head_off, L * kD * 2);
+  const unsigned char* k_head = k + head_off;
+  const unsigned char* v_head = v + head_off;
   const int32_t* sel = block_idx + ((size_t)bh * n_blocks + qb) * topk;
   auto tile_block = [&](int t) { return min(max(sel[t], 0), n_blocks - 1); };
 
   // ---- Q^T operand: lane holds Q[query n][16*ks + 8*h + 0..7] for ks = 0..7
   // (rows past the end of a short last block load the last row and are not stored)
   const int qrow = block_first_token<kCube>(geom, qb) + row_token_offset<kCube>(geom, qg * 32 + n);
-  // byte offset, from a tile's first token, of this lane's row in each of its copy segments
-  int rowb[4];
+  // byte offset, from a tile's first token, of the 16 bytes this lane copies in each of
+  // its copy segments (its row, and the logical chunk the swizzle puts at lane%16)
+  int laneoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rowb[i] = row_token_offset<kCube>(geom, 4 * (wave + 8 * i) + (lane >> 4)) * kD * 2;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (wave + 8 * i) + (lane >> 4);
+    laneoff[i] = row_token_offset<kCube>(geom, row) * kD * 2 + (((lane & 15) ^ swz(row)) << 4);
+  }
   auto tile_off = [&](int j) { return block_first_token<kCube>(geom, j) * kD * 2; };
+  // bytes a tile starting at byte `off` may read: 128 rows (fewer for a short last block);
+  // a box's rows are spread over the head, which it never passes
+  const int head_bytes = L * kD * 2;
+  auto tile_bytes = [&](int off) { return kCube ? head_bytes - off : min(head_bytes - off, kTileBytes); };
+  auto k_tile = [&](int off) { return tile_rsrc(k_head, off, tile_bytes(off)); };
+  auto v_tile = [&](int off) { return tile_rsrc(v_head, off, tile_bytes(off)); };
   bf16x8 qf[8];
   {
     const unsigned char* qp = q + head_off + (size_t)min(qrow, L - 1) * kD * 2;
@@ -267,129 +316,160 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
   for (int md = 0; md < 4; ++md) o[md] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16 st[2];         // S^T of the tile this wave scores next
+  uint32_t pb[4][4];    // P^T operand (8 bf16 = 4 dwords per k-step) of the tile it accumulates next
 
-  // ---- prologue: K0, K1, K2 and V0 into LDS; S_0
-  // K(j) lives in K buffer j%3 and is read in step j-1 (for S_j), V(j) in V buffer j%2,
-  // read in step j.  Step t refills the V buffer of V(t-1) with V(t+1), issued after the
-  // softmax, and the K buffer of K(t) (read in step t-1) with K(t+3), one quarter per
-  // k-step of the P.V products; so V's copies precede K's, and the wait opening step
-  // t+1 (vmcnt <= 4) leaves only this wave's four K(t+3) copies in flight.  Past the end
-  // of the list the last tile is copied again into the free buffer (never read),
-  // keeping the number of copies per step fixed.
-  auto blk = [&](int t) { return tile_block(min(t, topk - 1)); };
-  tile_dma(kbuf(0), k_rsrc, tile_off(blk(0)), rowb, wave, lane);
-  tile_dma(vbuf(0), v_rsrc, tile_off(blk(0)), rowb, wave, lane);
-  tile_dma(kbuf(1), k_rsrc, tile_off(blk(1)), rowb, wave, lane);
-  tile_dma(kbuf(2), k_rsrc, tile_off(blk(2)), rowb, wave, lane);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));      // K0 and V0 landed (K1, K2 may fly)
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  compute_st(sa, kbuf(0), key0, qf, n, h);
-
-  int cur_blk = blk(0);   // block of tile t, read (scalar) by the step before: no vector load in the loop
-  // byte offsets of the tiles a step copies (V(t+1), K(t+3)), computed during the
-  // previous step's products rather than at the top of the step
-  int v_next_off = tile_off(blk(1)), k3_next_off = tile_off(blk(3));
-  auto step = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int t, unsigned char* k_next, unsigned char* k_free,
-                  unsigned char* v_cur, unsigned char* v_free) __attribute__((always_inline)) {
-    const bool has_next = t + 1 < topk;
-    const int this_blk = cur_blk;
-    const int next_blk = blk(t + 1);
-    cur_blk = next_blk;
-    // this wave's copies of K(t+1) and V(t) have landed (only its four copies of
-    // K(t+2), the youngest, may still be in flight) and its LDS reads are done; after
-    // the barrier every wave's copies are in LDS and every wave is done with K(t)
-    // (read for S_t in step t-1) and V(t-1), whose buffers this step refills
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int k3_off = k3_next_off, v_off = v_next_off;
-    // key half 0 computes the next S first, key half 1 after its softmax
-    if (kh == 0 && has_next) compute_st(snext, k_next, key0, qf, n, h);
-
-    // softmax on S_t (log2 domain)
-    const int valid = kCube ? kBlock : L - this_blk * kBlock;   // keys that exist (short last block)
-    if (valid < kBlock) mask_missing_keys(scur, key0, h, valid);
-    float mx = scur[0][0];
+  // Softmax of the scores in st for key block `tb` (log2 domain): p = 2^(s*scale_log2 - m_run)
+  // against the running max, rounded to bf16 into pb.  The max is not recomputed per tile:
+  // any m works (the common factor 2^-m cancels between O and l) as long as no weight
+  // overflows.  So the weights are formed with the current m_run, and only if some lane's
+  // sum of its 32 weights exceeds 2^15 (or is not finite: the first tile, where m_run =
+  // -inf) does the wave take the exact path -- row max, m_run raised to it, O and l
+  // rescaled, weights formed again (then <= 1).  Every weight stays <= 2^15.
+  auto softmax_tile = [&](int tb) __attribute__((always_inline)) {
+    const int valid = kCube ? kBlock : L - tb * kBlock;   // keys that exist (short last block)
+    if (valid < kBlock) mask_missing_keys(st, key0, h, valid);
+    float lsum = softmax_weights(st, scale_log2, m_run, pb);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(lsum <= 32768.f)) != 0, 0)) {
+      float mx = st[0][0];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // a key half with no existing key yet keeps m = -inf, weights 0 and alpha 1
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-    float lsum = 0.f;
-    uint32_t pb[4][4];   // P^T operand per k-step (8 bf16 = 4 dwords)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r], scale_log2, -m_sub));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[mb][r + 1], scale_log2, -m_sub));
-        lsum += p0 + p1;
-        const int ks = 2 * mb + (r >> 3);
-        const int dw = ((r >> 2) & 1) * 2 + ((r & 3) >> 1);
-        pb[ks][dw] = pack_bf16x2(p0, p1);
-      }
-    }
-    l_run = l_run * alpha + lsum;
-    if (__ballot(alpha != 1.f)) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // a key half with no existing key yet keeps m = -inf, weights 0 and alpha 1
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int md = 0; md < 4; ++md)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+      lsum = softmax_weights(st, scale_log2, m_new == -INFINITY ? 0.f : m_new, pb);
     }
-
-    tile_dma(v_free, v_rsrc, v_off, rowb, wave, lane);   // V copies after the softmax
-    if (kh == 1 && has_next) compute_st(snext, k_next, key0, qf, n, h);
-
-    // O^T += V^T P^T over this wave's 64 keys
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      tile_dma_seg(k_free, k_rsrc, k3_off, rowb, wave, lane, ks);   // one K copy per k-step
-      if (ks == 0) {
-        v_next_off = tile_off(blk(t + 2));
-        k3_next_off = tile_off(blk(t + 4));
-      }
-      const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]});
-      const unsigned char* vk = v_cur + ks * 16 * 256;
-#pragma unroll
-      for (int md = 0; md < 4; ++md) {
-        const i16x4 lo = ds_read_tr(vk, tr_off[0][md]);
-        const i16x4 hi = ds_read_tr(vk, tr_off[1][md]);
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[md], 0, 0, 0);
-      }
-    }
-    // transposed V reads run three products ahead (two reads per product)
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 1);
-#pragma unroll
-    for (int i = 0; i < 13; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 1);
+    l_run += lsum;
   };
 
-  // six steps per round: K buffers cycle with period 3, V buffers and S registers with 2
-  for (int t = 0; t < topk; t += 6) {
-    step(sa, sb, t, k1s, k0s, v0s, v1s);
-    if (t + 1 >= topk) break;
-    step(sb, sa, t + 1, k2s, k1s, v1s, v0s);
-    if (t + 2 >= topk) break;
-    step(sa, sb, t + 2, k0s, k2s, v0s, v1s);
-    if (t + 3 >= topk) break;
-    step(sb, sa, t + 3, k1s, k0s, v1s, v0s);
-    if (t + 4 >= topk) break;
-    step(sa, sb, t + 4, k2s, k1s, v0s, v1s);
-    if (t + 5 >= topk) break;
-    step(sb, sa, t + 5, k0s, k2s, v1s, v0s);
-  }
+  // ---- prologue: K0, K1, K2 and V0 into LDS; S_0 (and, for key half 0, P_0)
+  // K(j) lives in K buffer j%3 and is read in step j-1 (for S_j), V(j) in V buffer j%2,
+  // read in step j.  Step t refills the V buffer of V(t-1) with V(t+1) and the K buffer of
+  // K(t) (read in step t-1) with K(t+3), one quarter per k-step of the P.V products; V's
+  // copies are issued first, so the wait opening step t+1 (vmcnt <= 4) leaves only this
+  // wave's four K(t+3) copies in flight.  Past the end of the list the last tile is
+  // copied again into the free buffer (never read), keeping the copies per step fixed.
+  auto blk = [&](int t) { return tile_block(min(t, topk - 1)); };
+  tile_dma(kbuf(0), k_tile(tile_off(blk(0))), laneoff, wave);
+  tile_dma(vbuf(0), v_tile(tile_off(blk(0))), laneoff, wave);
+  tile_dma(kbuf(1), k_tile(tile_off(blk(1))), laneoff, wave);
+  tile_dma(kbuf(2), k_tile(tile_off(blk(2))), laneoff, wave);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));      // K0 and V0 landed (K1, K2 may fly)
+  __syncthreads();
+  compute_st(st, kbuf(0), key0, qf, n, h);
+  int cur_blk = blk(0);   // block of tile t, read (scalar) by the step before: no vector load in the loop
+
+
+  // Step t in two halves separated by a barrier.  In each half one wave of a SIMD's pair
+  // runs its matrix phase -- S_{t+1} = K(t+1) Q^T and O^T += V(t)^T P_t^T, 32 products --
+  // at raised issue priority, while the other runs its vector phase (the softmax of the
+  // tile it accumulates next); the roles swap in the second half.  Key half 0 takes the
+  // matrix phase first (its P_t was formed in the previous step's second half), key half
+  // 1 second (its P_t is formed in the first half).  The barrier keeps the pair in
+  // opposite phases: without it the older wave wins issue arbitration, runs ahead, and
+  // the pair ends each step with one wave alone on the SIMD.  The loop is compiled once
+  // per key half (KH), so each wave runs straight-line code for its own role.
+  auto run = [&](auto khc) __attribute__((always_inline)) {
+    constexpr int KH = decltype(khc)::value;
+    if (KH == 0) softmax_tile(cur_blk);
+
+    auto matrix_phase = [&](int t, bool has_next, int k3_off, unsigned char* k_next, unsigned char* k_free,
+                            unsigned char* v_cur) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      if (has_next) compute_st(st, k_next, key0, qf, n, h);
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T P^T over this wave's 64 keys
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]});
+        const unsigned char* vk = v_cur + ks * 16 * 256;
+#pragma unroll
+        for (int md = 0; md < 4; ++md) {
+          const i16x4 lo = ds_read_tr(vk, tr_off[0][md]);
+          const i16x4 hi = ds_read_tr(vk, tr_off[1][md]);
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[md], 0, 0, 0);
+        }
+      }
+      // transposed V reads run kVAhead products ahead (two reads per product)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVAhead, 1);
+#pragma unroll
+      for (int i = 0; i < 16 - kVAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kVAhead, 1);
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    auto step = [&](int t, unsigned char* k_next, unsigned char* k_free, unsigned char* v_cur,
+                    unsigned char* v_free) __attribute__((always_inline)) {
+      const bool has_next = t + 1 < topk;
+      const int blk_t = cur_blk;
+      // The step's block indices are scalar loads issued before the wait below, which
+      // already drains the scalar/LDS counter: loaded later, their own wait would also
+      // drain the operand reads running ahead of the products.
+      const int blk_t1 = blk(t + 1);
+      const int blk_t3 = blk(t + 3);
+      cur_blk = blk_t1;
+      // this wave's copies of K(t+1) and V(t) have landed (only its four copies of
+      // K(t+2), the youngest, may still be in flight) and its LDS reads are done; after
+      // the barrier every wave's copies are in LDS and every wave is done with K(t)
+      // (read for S_t in step t-1) and V(t-1), whose buffers this step refills
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int k3_off = tile_off(blk_t3), v_off = tile_off(blk_t1);
+      auto mid_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (KH == 0) {
+        matrix_phase(t, has_next, k3_off, k_next, k_free, v_cur);
+        mid_barrier();
+        tile_dma(v_free, v_tile(v_off), laneoff, wave);
+        if (has_next) softmax_tile(blk_t1);          // P_{t+1}
+        tile_dma(k_free, k_tile(k3_off), laneoff, wave);
+      } else {
+        tile_dma(v_free, v_tile(v_off), laneoff, wave);
+        softmax_tile(blk_t);                          // P_t
+        tile_dma(k_free, k_tile(k3_off), laneoff, wave);
+        mid_barrier();
+        matrix_phase(t, has_next, k3_off, k_next, k_free, v_cur);
+      }
+    };
+
+    // six steps per round: K buffers cycle with period 3, V buffers with 2
+    for (int t = 0; t < topk; t += 6) {
+      step(t, k1s, k0s, v0s, v1s);
+      if (t + 1 >= topk) break;
+      step(t + 1, k2s, k1s, v1s, v0s);
+      if (t + 2 >= topk) break;
+      step(t + 2, k0s, k2s, v0s, v1s);
+      if (t + 3 >= topk) break;
+      step(t + 3, k1s, k0s, v1s, v0s);
+      if (t + 4 >= topk) break;
+      step(t + 4, k2s, k1s, v0s, v1s);
+      if (t + 5 >= topk) break;
+      step(t + 5, k0s, k2s, v1s, v0s);
+    }
+  };
+  if (kh == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
   // every copy landed and every wave done with the tile buffers before they are reused
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __syncthreads();
