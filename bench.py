@@ -31,12 +31,13 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 2.4 GHz x 
 PEAK_HBM_GBS = 8000.0
 
 # Memory-side traffic of one sol_attn_fwd launch on the headline workload (bytes):
-# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are
-# what the same counters read for a plain copy of known size in the same command).
+# rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are what
+# the same counters read for the pool kernel in the same command, which reads Q and K
+# once and writes the pooled means: profiles/fwd_bf16_refine_1344x768.md).
 # The figure belongs to the kernel source whose SHA-256 prefix is stored beside it:
 # when csrc/fwd_bf16.hip differs, the traffic is reported as null until re-measured.
-FWD_TRAFFIC_BYTES = 47765202771
-FWD_TRAFFIC_SRC_SHA256 = "f4224e96746dcba0"   # the source as measured (its last change since was a comment)
+FWD_TRAFFIC_BYTES = 42330755243
+FWD_TRAFFIC_SRC_SHA256 = "eecf44144f55331b"
 FWD_SRC = os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", "fwd_bf16.hip")
 
 
