@@ -25,11 +25,20 @@ patterns) or to fp32.
 Random streams: numpy PCG64 seeded with SeedSequence(seed); it spawns one child
 per tensor (Q, K, V), and each child spawns one grandchild per (b, h).  Inside a
 head the coarse field [d, Tc, hc, wc] is drawn first, then the noise [L, d].
+
+Cache: when a cache directory is named (the `cache_dir` argument, else the
+SOL_ATTN_CACHE_DIR environment variable; unset or empty means no cache), make_qkv
+stores each tensor's bits as a plain .npy file named by `input_key` -- a hash of
+every field of the workload and GENERATOR_VERSION -- and later calls with the same
+key load them instead of generating.  Bump GENERATOR_VERSION whenever the values
+this module produces change, so that stale files are never read.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import dataclasses
+import hashlib
+import json
 import math
 import os
 from typing import Dict, Optional, Sequence, Tuple
@@ -38,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "make_qkv", "make_tensor", "f64_to_bf16_bits",
-    "bf16_bits_to_f32", "GENERATOR_VERSION",
+    "bf16_bits_to_f32", "GENERATOR_VERSION", "input_key", "cache_dir_from_env",
 ]
 
 GENERATOR_VERSION = 1
@@ -203,6 +212,60 @@ def make_tensor(wl: Workload, which: int, heads: Optional[Sequence[int]] = None)
     return res
 
 
-def make_qkv(wl: Workload):
-    """(Q, K, V) stored bits for the workload, each [B,H,L,d]."""
-    return tuple(make_tensor(wl, i) for i in range(3))
+def input_key(wl: Workload) -> str:
+    """Hex key naming the generated tensors: every workload field plus GENERATOR_VERSION."""
+    fields = dataclasses.asdict(wl)
+    fields["generator_version"] = GENERATOR_VERSION
+    blob = json.dumps(fields, sort_keys=True, separators=(",", ":"))
+    return hashlib.sha256(blob.encode()).hexdigest()[:24]
+
+
+def cache_dir_from_env() -> Optional[str]:
+    d = os.environ.get("SOL_ATTN_CACHE_DIR", "")
+    return d or None
+
+
+def _expected(wl: Workload):
+    return (wl.B, wl.H, wl.L, wl.d), np.dtype(np.uint16 if wl.dtype == "bf16" else np.float32)
+
+
+def _load_cached(path: str, wl: Workload) -> Optional[np.ndarray]:
+    """The cached tensor, or None when the file is missing or does not have the workload's shape/type."""
+    if not os.path.exists(path):
+        return None
+    try:
+        x = np.load(path, allow_pickle=False)
+    except (OSError, ValueError):
+        return None
+    shape, dtype = _expected(wl)
+    return x if x.shape == shape and x.dtype == dtype else None
+
+
+def _store(path: str, x: np.ndarray) -> None:
+    """Write through a temporary name and rename, so a reader never sees half a file."""
+    tmp = f"{path}.{os.getpid()}.tmp"
+    with open(tmp, "wb") as f:
+        np.save(f, x, allow_pickle=False)
+    os.replace(tmp, path)
+
+
+def make_qkv(wl: Workload, cache_dir: Optional[str] = None):
+    """(Q, K, V) stored bits for the workload, each [B,H,L,d].
+
+    With a cache directory (argument, else SOL_ATTN_CACHE_DIR) the tensors are read
+    from / written to <dir>/inputs/<input_key>_{q,k,v}.npy."""
+    cache_dir = cache_dir or cache_dir_from_env()
+    if cache_dir is None:
+        return tuple(make_tensor(wl, i) for i in range(3))
+    sub = os.path.join(cache_dir, "inputs")
+    os.makedirs(sub, exist_ok=True)
+    key = input_key(wl)
+    out = []
+    for i, tag in enumerate("qkv"):
+        path = os.path.join(sub, f"{key}_{tag}.npy")
+        x = _load_cached(path, wl)
+        if x is None:
+            x = make_tensor(wl, i)
+            _store(path, x)
+        out.append(x)
+    return tuple(out)

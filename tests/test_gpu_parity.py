@@ -8,6 +8,7 @@ launch configuration the benchmark times and are checked on sampled query blocks
 """
 import concurrent.futures as cf
 import dataclasses
+import hashlib
 import math
 import os
 
@@ -17,6 +18,7 @@ import torch
 
 import oracle
 from block_sparse_attention_attn_amd import workloads as W
+from oracle_cache import cached
 
 pytestmark = pytest.mark.gpu
 
@@ -259,6 +261,26 @@ def sampled_attention(Qd, Kd, Vd, sel, block, picks_per_head):
         return dict(ex.map(one, jobs))
 
 
+def cached_sampled_attention(wl, kind, Qf, Kf, Vf, sel, picks_per_head):
+    """sampled_attention through the oracle-result cache (keyed by the workload, the
+    selection's hash and the sampled blocks)."""
+    params = {"sel": hashlib.sha256(np.ascontiguousarray(sel).tobytes()).hexdigest()[:16],
+              "picks": [list(map(int, p)) for p in picks_per_head]}
+
+    def compute():
+        ref = sampled_attention(Qf, Kf, Vf, sel, wl.block, picks_per_head)
+        arrays = {}
+        for (bh, i), (Oi, lsei) in ref.items():
+            arrays[f"O_{bh}_{i}"], arrays[f"lse_{bh}_{i}"] = Oi, lsei
+        return arrays
+
+    arrays, hit = cached(wl, kind, params, compute)
+    if hit:
+        log(f"{kind}: oracle rows from the cache")
+    return {(bh, i): (arrays[f"O_{bh}_{i}"], arrays[f"lse_{bh}_{i}"])
+            for bh, p in enumerate(picks_per_head) for i in p}
+
+
 def check_sampled(out, lse, ref, L, block, what):
     o = out.view(-1, L, out.shape[-1])
     ls = lse.view(-1, L)
@@ -304,12 +326,18 @@ def test_full_size_workload(S, name):
     del out2, lse2
     log(f"full {name}: oracle pool/select")
     Qd = oracle.widen(q, "bf16")
-    qbar = oracle.pool(Qd, wl.block)
-    assert np.array_equal(qp.cpu().numpy(), qbar)
     Kd = oracle.widen(k, "bf16")
-    kbar = oracle.pool(Kd, wl.block)
-    assert np.array_equal(kp.cpu().numpy(), kbar)
-    want = oracle_select_parallel(qbar, kbar, wl.topk)
+
+    def pool_select():
+        qbar, kbar = oracle.pool(Qd, wl.block), oracle.pool(Kd, wl.block)
+        return {"qbar": qbar, "kbar": kbar, "idx": oracle_select_parallel(qbar, kbar, wl.topk)}
+
+    ps, hit = cached(wl, "pool_select", {"topk": wl.topk}, pool_select)
+    if hit:
+        log(f"full {name}: oracle pool/select from the cache")
+    assert np.array_equal(qp.cpu().numpy(), ps["qbar"])
+    assert np.array_equal(kp.cpu().numpy(), ps["kbar"])
+    want = ps["idx"]
     got = idx.cpu().numpy()
     assert np.array_equal(got, want)
     # every output row written, finite
@@ -320,7 +348,7 @@ def test_full_size_workload(S, name):
     Qf, Kf, Vf = (x.reshape(BH, wl.L, wl.d) for x in (Qd, Kd, Vd))
     rng = np.random.default_rng(wl.seed)
     picks = [sample_blocks(nb, order, rng) for _ in range(BH)]
-    ref = sampled_attention(Qf, Kf, Vf, want.reshape(BH, nb, wl.topk), wl.block, picks)
+    ref = cached_sampled_attention(wl, "sampled", Qf, Kf, Vf, want.reshape(BH, nb, wl.topk), picks)
     check_sampled(out, lse, ref, wl.L, wl.block, f"full {name}")
     if name == "refine_2k":
         # the dense (k = all blocks) run, into freshly NaN-filled outputs
@@ -337,5 +365,5 @@ def test_full_size_workload(S, name):
         dense = np.broadcast_to(np.arange(kd, dtype=np.int32), (BH, nb, kd))
         rng = np.random.default_rng(44)
         picks = [sample_blocks(nb, order, rng, extra=0) for _ in range(BH)]
-        ref = sampled_attention(Qf, Kf, Vf, dense, wl.block, picks)
+        ref = cached_sampled_attention(wl, "sampled_dense", Qf, Kf, Vf, dense, picks)
         check_sampled(out, lse, ref, wl.L, wl.block, "full refine_2k dense")
