@@ -29,10 +29,26 @@
 //      j.  With interleaved ownership, ascending j is (t, lane) order, so a key's
 //      output position is a running count plus the popcount of the ballot bits
 //      of lower lanes: the output comes out ascending without a sort or scan.
+#include <atomic>
+
 #include "launchers.h"
 
 namespace sol_attn {
 namespace {
+
+// Allow a kernel the whole 160 KiB of dynamic LDS, once per device and kernel (the attribute
+// is per function and device).  Later launches then make no call besides the launch itself,
+// so a stream that is being captured into a graph records only kernel nodes.
+__host__ hipError_t allow_full_lds(const void* kernel, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (err == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return err;
+}
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -316,8 +332,10 @@ hipError_t launch_select_mfma(const double* q_pooled, const double* k_pooled, in
             : per_lane <= 16 ? (wide ? select_mfma_kernel<16, kS, 8> : select_mfma_kernel<16, kS, 4>)
             : select_mfma_kernel<(kMaxMfmaBlocks + 63) / 64, kS, 8>;
   const int threads = wide ? 8 * 64 : 4 * 64;
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // one flag word per instantiation that can be chosen here
+  static std::atomic<uint64_t> done[5];
+  const int which = per_lane <= 4 ? 0 : per_lane <= 8 ? 1 : per_lane <= 16 ? (wide ? 2 : 3) : 4;
+  hipError_t err = allow_full_lds(reinterpret_cast<const void*>(kern), done[which]);
   if (err != hipSuccess) {
     (void)hipGetLastError();
     return err;
@@ -347,8 +365,8 @@ hipError_t launch_select(const double* q_pooled, const double* k_pooled, int BH,
   const size_t lds = select_lds_bytes(rows, n_blocks, d);
   if (lds > budget) return hipErrorInvalidValue;
   dim3 grid((n_blocks + rows - 1) / rows, BH);
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> done{0};
+  hipError_t err = allow_full_lds(reinterpret_cast<const void*>(select_kernel), done);
   if (err != hipSuccess) {
     (void)hipGetLastError();
     return err;

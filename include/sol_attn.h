@@ -33,11 +33,18 @@
  * The block index list is int32 [B, H, n_blocks, topk], ascending per row.
  *
  * Ownership and execution.  Every pointer argument is a DEVICE pointer owned by
- * the caller; the library allocates no memory, keeps no state between calls and
- * never retains a pointer.  Calls enqueue their kernel(s) on `stream` (a
- * hipStream_t; NULL = the default stream) and return without synchronising;
- * results are valid once the stream has reached that point.  Outputs must not
- * alias inputs.  Calls are thread-safe.
+ * the caller; the library allocates no memory and never retains a pointer.  Its only
+ * state is one flag per device and select kernel: the first sol_attn_select on a
+ * device raises that kernel's dynamic-LDS limit once.  Calls enqueue their kernel(s)
+ * on `stream` (a hipStream_t; NULL = the default stream) and return without
+ * synchronising; results are valid once the stream has reached that point.  Outputs
+ * must not alias inputs.  Calls are thread-safe.
+ *
+ * Graph capture.  The device calls record kernel launches only (no allocation, memset
+ * or copy), so a sequence of them -- e.g. pool, select, fwd -- can be captured into a
+ * HIP graph from `stream` and replayed; a replay reads the inputs' current contents.
+ * Make one sol_attn_select call on the device before capturing, so that the one-time
+ * attribute change above happens outside the capture.
  *
  * Errors.  Argument errors are detected on the host before anything is enqueued
  * and leave every output untouched.  A failure reported by the HIP runtime at
