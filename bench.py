@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,16 +35,25 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (KiB per dispatch; the factors are what
 # the same counters read for the pool kernel in the same command, which reads Q and K
 # once and writes the pooled means: profiles/fwd_bf16_refine_1344x768.md).
-# The figure belongs to the kernel source whose SHA-256 prefix is stored beside it:
-# when csrc/fwd_bf16.hip differs, the traffic is reported as null until re-measured.
+# The figure belongs to the kernel code whose SHA-256 prefix is stored beside it (the code
+# of csrc/fwd_bf16.hip with comments removed and whitespace collapsed): when the code
+# differs, the traffic is reported as null until re-measured.
 FWD_TRAFFIC_BYTES = 42330755243
-FWD_TRAFFIC_SRC_SHA256 = "eecf44144f55331b"
+FWD_TRAFFIC_SRC_SHA256 = "58087810071fd57e"
 FWD_SRC = os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", "fwd_bf16.hip")
+_C_COMMENT_OR_LITERAL = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'', re.S)
+
+
+def code_sha(text: str) -> str:
+    """SHA-256 prefix of C/C++ source with comments removed and whitespace collapsed
+    (string and character literals are kept as written)."""
+    code = _C_COMMENT_OR_LITERAL.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()[:16]
 
 
 def fwd_source_sha() -> str:
-    with open(FWD_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(FWD_SRC, encoding="utf-8") as f:
+        return code_sha(f.read())
 
 
 def fwd_traffic_bytes():
