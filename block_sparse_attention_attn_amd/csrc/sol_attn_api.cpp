@@ -98,6 +98,8 @@ sol_attn_status_t sol_attn_fwd(const void* q, const void* k, const void* v, sol_
                                float softmax_scale, void* out, float* lse_or_null, void* stream) {
   sol_attn_status_t st = check_common(dtype, B, H, L, d, block);
   if (st != SOL_ATTN_OK) return st;
+  if (std::isinf(softmax_scale) && softmax_scale > 0.f)
+    return fail(SOL_ATTN_ERR_SHAPE, "fwd: softmax_scale must be finite");
   const bool bf16 = dtype == SOL_ATTN_BF16;
   if (bf16 && !(d == 128 && block == 128))
     return fail(SOL_ATTN_ERR_UNSUPPORTED, "bf16 fwd needs d == 128 and block == 128 (d=%d block=%d)", d, block);
@@ -201,6 +203,8 @@ sol_attn_status_t sol_attn_fwd_cube(const void* q, const void* k, const void* v,
   long long L = 0;
   sol_attn_status_t st = check_cube("fwd_cube", B, H, T, h, w, bt, by, bx, &L);
   if (st != SOL_ATTN_OK) return st;
+  if (std::isinf(softmax_scale) && softmax_scale > 0.f)
+    return fail(SOL_ATTN_ERR_SHAPE, "fwd_cube: softmax_scale must be finite");
   if ((long long)bt * by * bx != 128)
     return fail(SOL_ATTN_ERR_UNSUPPORTED, "fwd_cube needs boxes of 128 tokens (box %dx%dx%d)", bt, by, bx);
   const long long BH = (long long)B * H;

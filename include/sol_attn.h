@@ -75,7 +75,7 @@ typedef enum {
 typedef enum {
   SOL_ATTN_OK = 0,
   SOL_ATTN_ERR_NULL = 1,        /* a required pointer is NULL                          */
-  SOL_ATTN_ERR_SHAPE = 2,       /* negative size, or d/block <= 0                      */
+  SOL_ATTN_ERR_SHAPE = 2,       /* negative size, d/block <= 0, or infinite scale      */
   SOL_ATTN_ERR_K = 3,           /* topk < 1 or topk > n_blocks                         */
   SOL_ATTN_ERR_UNSUPPORTED = 4, /* dtype / d / block combination not built (see calls) */
   SOL_ATTN_ERR_ALIGN = 5,       /* pointer not aligned as the call requires            */
@@ -130,7 +130,8 @@ sol_attn_status_t sol_attn_select(const double* q_pooled, const double* k_pooled
  *                  tiles are re-read from cache rather than memory -- never the results.
  *                  NULL = ascending.  Entries outside [0, n_blocks) are clamped; a non-
  *                  permutation leaves some output rows unwritten.  See sol_attn_frame_order.
- *   softmax_scale  multiplier of q.k inside the softmax; <= 0 selects 1/sqrt(d).
+ *   softmax_scale  multiplier of q.k inside the softmax; a value <= 0 or NaN selects
+ *                  1/sqrt(d); +infinity is rejected with SOL_ATTN_ERR_SHAPE.
  *   out            [B,H,L,d] of `dtype`: O = softmax(q K_sel^T * scale) V_sel per query row;
  *                  bf16 results are rounded to nearest-even from float32.
  *   lse_or_null    optional float32 [B,H,L]: natural-log log-sum-exp of the scaled logits.

@@ -38,8 +38,8 @@ MIS = FAKE + 2      # misaligned
 
 
 def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, dtype=0, B=1, H=1, L=256, d=128, block=128, topk=1, idx=FAKE,
-         out=FAKE, lse=None, order=None):
-    return lib.sol_attn_fwd(q, k, v, dtype, B, H, L, d, block, topk, idx, order, 0.0, out, lse, None)
+         out=FAKE, lse=None, order=None, scale=0.0):
+    return lib.sol_attn_fwd(q, k, v, dtype, B, H, L, d, block, topk, idx, order, scale, out, lse, None)
 
 
 def test_fwd_argument_errors(lib):
@@ -60,6 +60,9 @@ def test_fwd_argument_errors(lib):
     assert _fwd(lib, lse=FAKE + 2) == 5
     assert _fwd(lib, order=FAKE + 1) == 5
     assert b"topk" in lib.sol_attn_last_error() or b"aligned" in lib.sol_attn_last_error()
+    assert _fwd(lib, scale=float("inf")) == 2
+    assert b"softmax_scale" in lib.sol_attn_last_error()
+    assert _fwd(lib, scale=float("inf"), B=0) == 2     # an argument error even with nothing to do
 
 
 def test_fwd_empty_problem_is_a_noop(lib):
@@ -179,6 +182,8 @@ def test_fwd_cube_argument_checks(lib):
     assert f(out=MIS) == 5
     assert f(lse=FAKE + 2) == 5
     assert f(order=FAKE + 1) == 5
+    assert lib.sol_attn_fwd_cube(FAKE, FAKE, FAKE, 1, 1, 4, 16, 16, 2, 8, 8, 2, FAKE, None, float("inf"), FAKE,
+                                 None, None) == 2
     assert f(B=0, q=None, idx=None) == 0       # nothing to do
     assert f(T=0, topk=99) == 0
     assert lib.sol_attn_last_error() == b""
