@@ -116,6 +116,16 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _check_on_device(device: torch.device, **tensors: Optional[torch.Tensor]):
+    """Every given tensor (None = absent) lives on `device`, a HIP device: the kernels
+    dereference these pointers, and a host or other-device pointer would fault there."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a HIP device, not {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} must be on {device} (it is on {t.device})")
+
+
 def _check_qkv(*ts: torch.Tensor):
     ref = ts[0]
     if ref.dim() != 4:
@@ -145,8 +155,10 @@ def sol_attn_select(q_pooled: torch.Tensor, k_pooled: torch.Tensor, topk: int, r
     lib = load_library()
     if q_pooled.dtype != torch.float64 or k_pooled.dtype != torch.float64:
         raise TypeError("pooled tensors must be float64")
-    if q_pooled.shape != k_pooled.shape or not (q_pooled.is_contiguous() and k_pooled.is_contiguous()):
+    if (q_pooled.dim() != 4 or q_pooled.shape != k_pooled.shape
+            or not (q_pooled.is_contiguous() and k_pooled.is_contiguous())):
         raise ValueError("pooled tensors must be contiguous [B,H,nB,d] of equal shape")
+    _check_on_device(q_pooled.device, k_pooled=k_pooled)
     B, H, nb, d = q_pooled.shape
     idx = torch.empty((B, H, nb, max(topk, 0)), dtype=torch.int32, device=q_pooled.device)
     scores = torch.empty((B, H, nb, nb), dtype=torch.float64, device=q_pooled.device) if return_scores else None
@@ -198,6 +210,7 @@ def sol_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: t
     B, H, L, d = q.shape
     if block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4:
         raise ValueError("block_idx must be contiguous int32 [B,H,nB,topk]")
+    _check_on_device(q.device, block_idx=block_idx, out=out, lse=lse, qblock_order=qblock_order)
     topk = block_idx.shape[-1]
     if block > 0 and tuple(block_idx.shape[:3]) != (B, H, -(-L // block)):
         raise ValueError("block_idx leading dims must be [B,H,L/block]")
@@ -293,11 +306,14 @@ def sol_attn_fwd_cube(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_i
     bt, by, bx = cube
     if block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4:
         raise ValueError("block_idx must be contiguous int32 [B,H,n_boxes,topk]")
+    _check_on_device(q.device, block_idx=block_idx, out=out, qblock_order=qblock_order)
     nb = L // (bt * by * bx) if min(bt, by, bx) > 0 else 0
     if tuple(block_idx.shape[:3]) != (B, H, nb):
         raise ValueError("block_idx leading dims must be [B,H,n_boxes]")
     if out is None:
         out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
     if qblock_order is not None:
         if (qblock_order.dtype != torch.int32 or qblock_order.device != q.device or qblock_order.numel() != nb
@@ -368,8 +384,11 @@ def sol_attn_dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: int,
     B, H, L, d = codes.shape
     if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, L) or not scales.is_contiguous():
         raise ValueError("scales must be contiguous float32 [B,H,L]")
+    _check_on_device(codes.device, scales=scales, out=out)
     if out is None:
         out = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=codes.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, L, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [B,H,L,d] tensor")
     _check("sol_attn_dequantize", lib.sol_attn_dequantize(_ptr(codes), _ptr(scales), B, H, L, d, fmt, _ptr(out),
                                                           _stream(codes)))
     return out

@@ -104,11 +104,34 @@ def test_select_argument_errors(lib):
     assert s(nb=0, topk=0) == 0
 
 
+def test_binding_device_check():
+    """Every pointer a kernel dereferences must be on the call's HIP device: host tensors
+    and tensors on another device are refused before the library is called."""
+    import torch
+    cpu = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="HIP device"):
+        S._check_on_device(torch.device("cpu"), x=cpu)
+    dev0, dev1 = torch.device("cuda", 0), torch.device("cuda", 1)
+    with pytest.raises(ValueError, match="block_idx"):
+        S._check_on_device(dev0, block_idx=cpu, out=None)
+    meta = torch.empty(2, device="meta")
+    with pytest.raises(ValueError, match="lse"):
+        S._check_on_device(dev0, lse=meta)
+    S._check_on_device(dev0, out=None, lse=None)          # absent tensors are fine
+    assert dev0 != dev1
+
+
 def test_binding_refuses_cpu_tensors(lib):
     import torch
     q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         S.sol_attn_pool(q, q, 128)
+    qp = torch.zeros(1, 1, 4, 128, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        S.sol_attn_select(qp, qp, 2)
+    codes = torch.zeros(1, 1, 4, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        S.sol_attn_dequantize(codes, torch.ones(1, 1, 4), S.INT8)
 
 
 def test_frame_order(lib):

@@ -367,3 +367,26 @@ def test_full_size_workload(S, name):
         picks = [sample_blocks(nb, order, rng, extra=0) for _ in range(BH)]
         ref = cached_sampled_attention(wl, "sampled_dense", Qf, Kf, Vf, dense, picks)
         check_sampled(out, lse, ref, wl.L, wl.block, "full refine_2k dense")
+
+
+def test_binding_refuses_host_index_lists(S):
+    """An index list (or output) on the host with Q/K/V on the device is refused before any
+    launch: the kernels would otherwise dereference a host pointer."""
+    wl = dataclasses.replace(W.get("draft_896x512"), name="hostidx", H=1, frames=1, lat_h=8, lat_w=32,
+                             coarse=(1, 2, 2), topk=2, seed=5)
+    q, k, v = W.make_qkv(wl)
+    Q, K, V = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    idx = S.sol_attn_select(*S.sol_attn_pool(Q, K, 128), 2)
+    with pytest.raises(ValueError, match="block_idx"):
+        S.sol_attn_fwd(Q, K, V, idx.cpu(), 128)
+    with pytest.raises(ValueError, match="lse"):
+        S.sol_attn_fwd(Q, K, V, idx, 128, lse=torch.empty(1, 1, wl.L))
+    with pytest.raises(ValueError, match="block_idx"):
+        S.sol_attn_fwd_cube(Q, K, V, idx.cpu(), wl.grid, (1, 4, 32))
+    qp, kp = S.sol_attn_pool(Q, K, 128)
+    with pytest.raises(ValueError, match="k_pooled"):
+        S.sol_attn_select(qp, kp.cpu(), 2)
+    torch.cuda.synchronize()
+    out = S.sol_attn_fwd(Q, K, V, idx, 128)          # the same call with device tensors runs
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item()
