@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 # of csrc/fwd_bf16.hip with comments removed and whitespace collapsed): when the code
 # differs, the traffic is reported as null until re-measured.
 FWD_TRAFFIC_BYTES = 42330755243
-FWD_TRAFFIC_SRC_SHA256 = "58087810071fd57e"
+FWD_TRAFFIC_SRC_SHA256 = "51a3cbd0bf2c5870"
 FWD_SRC = os.path.join(ROOT, "block_sparse_attention_attn_amd", "csrc", "fwd_bf16.hip")
 _C_COMMENT_OR_LITERAL = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'', re.S)
 

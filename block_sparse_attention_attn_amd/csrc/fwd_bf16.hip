@@ -383,8 +383,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     constexpr int KH = decltype(khc)::value;
     if (KH == 0) softmax_tile(cur_blk);
 
-    auto matrix_phase = [&](int t, bool has_next, int k3_off, unsigned char* k_next, unsigned char* k_free,
-                            unsigned char* v_cur) __attribute__((always_inline)) {
+    auto matrix_phase = [&](bool has_next, unsigned char* k_next, unsigned char* v_cur)
+                            __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(1);
       if (has_next) compute_st(st, k_next, key0, qf, n, h);
       __builtin_amdgcn_sched_barrier(0);
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       };
       if (KH == 0) {
-        matrix_phase(t, has_next, k3_off, k_next, k_free, v_cur);
+        matrix_phase(has_next, k_next, v_cur);
         mid_barrier();
         tile_dma(v_free, v_tile(v_off), laneoff, wave);
         if (has_next) softmax_tile(blk_t1);          // P_{t+1}
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         softmax_tile(blk_t);                          // P_t
         tile_dma(k_free, k_tile(k3_off), laneoff, wave);
         mid_barrier();
-        matrix_phase(t, has_next, k3_off, k_next, k_free, v_cur);
+        matrix_phase(has_next, k_next, v_cur);
       }
     };
 

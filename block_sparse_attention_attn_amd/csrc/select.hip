@@ -105,11 +105,11 @@ __device__ __forceinline__ void topk_rows(const uint64_t* keys, int n_blocks, in
       const bool gt = j < n_blocks && x > T;
       const bool eq = j < n_blocks && x == T;
       const uint64_t eq_mask = __ballot(eq);
-      const bool take = gt || (eq && eq_seen + __popcll(eq_mask & below) < need_eq);
+      const bool take = gt || (eq && eq_seen + (int)__popcll(eq_mask & below) < need_eq);
       const uint64_t take_mask = __ballot(take);
       if (take) out[base + __popcll(take_mask & below)] = j;
       base += __popcll(take_mask);
-      eq_seen += __popcll(eq_mask);
+      eq_seen += (int)__popcll(eq_mask);
     }
   }
 }
@@ -149,11 +149,11 @@ __device__ __forceinline__ void topk_rows_reg(const uint64_t* keys, int n_blocks
       const bool gt = x[t] > T;
       const bool eq = x[t] == T && j < n_blocks;
       const uint64_t eq_mask = __ballot(eq);
-      const bool take = gt || (eq && eq_seen + __popcll(eq_mask & below) < need_eq);
+      const bool take = gt || (eq && eq_seen + (int)__popcll(eq_mask & below) < need_eq);
       const uint64_t take_mask = __ballot(take);
       if (take) out[base + __popcll(take_mask & below)] = j;
       base += __popcll(take_mask);
-      eq_seen += __popcll(eq_mask);
+      eq_seen += (int)__popcll(eq_mask);
     }
   }
 }
